@@ -1,0 +1,247 @@
+// api.hip -- host side of the C ABI: argument validation, variant choice on
+// the host (the "Xe2 ESIMD GEMM" page, "Inner-loop rules" and "SPIR-V linker
+// errors": runtime conditionals belong on the host, kernels are compile-time
+// variants) and the asynchronous launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/bpt_gemm.h"
+#include "gemm_generic.hpp"
+#include "gemm_pipelined.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bpt_status fail(bpt_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bpt_status fail(bpt_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+enum Variant {
+    V_AUTO = 0,
+    V_GENERIC = 1,          // guarded 64x64, any shape / alignment
+    V_PIPE_256 = 2,         // 256x256 tile, BK 64, 2 stages
+    V_PIPE_128 = 3,         // 128x128 tile, BK 64, 2 stages
+    V_COUNT = 3
+};
+
+const char* const kVariantNames[] = {
+    "auto",
+    "generic_64x64x16",
+    "pipelined_256x256x64_s2",
+    "pipelined_128x128x64_s2",
+};
+
+struct Call {
+    int dtype;
+    long long batch, M, N, K, lda, ldb, ldc, sA, sB, sC;
+    const void* A;
+    const void* B;
+    void* C;
+    int out_fp32;
+};
+
+constexpr long long kI31 = (1LL << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Can a pipelined variant with tile (BM, BN, BK) take this call?
+bool pipelined_ok(const Call& c, int BK) {
+    if (c.K <= 0 || c.K % BK != 0) return false;
+    if (!aligned16(c.A) || !aligned16(c.B)) return false;
+    if (c.lda % 8 != 0 || c.ldb % 8 != 0) return false;
+    if (c.sA % 8 != 0 || c.sB % 8 != 0) return false;
+    // buffer offsets are 32-bit: each operand's extent (plus one tile of
+    // rows past M) must stay below 2^31 bytes
+    long long extA = ((c.M + 256) * c.lda + c.K) * 2;
+    long long extB = (c.K * c.ldb + c.N + 256) * 2;
+    if (extA > kI31 || extB > kI31) return false;
+    return true;
+}
+
+int choose(const Call& c) {
+    if (!pipelined_ok(c, 64)) return V_GENERIC;
+    long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
+    return tiles256 >= 128 ? V_PIPE_256 : V_PIPE_128;
+}
+
+template <typename T, typename OutT, int BM, int BN>
+hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
+    bpt::GemmArgs a;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_m = (int)((c.M + BM - 1) / BM);
+    a.tiles_n = (int)((c.N + BN - 1) / BN);
+    a.group_m = 4;
+    const long long tiles = (long long)a.tiles_m * a.tiles_n;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        a.A = static_cast<const T*>(c.A) + b0 * c.sA;
+        a.B = static_cast<const T*>(c.B) + b0 * c.sB;
+        a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
+        hipLaunchKernelGGL((bpt::gemm_pipelined_kernel<T, BM, BN, 64, 2, 2, 2, OutT>),
+                           dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t launch_generic(const Call& c, hipStream_t stream) {
+    bpt::GenericArgs a;
+    a.M = c.M; a.N = c.N; a.K = c.K;
+    a.lda = c.lda; a.ldb = c.ldb; a.ldc = c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    const long long tm = (c.M + 63) / 64, tn = (c.N + 63) / 64;
+    a.tiles_n = (int)tn;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        a.A = static_cast<const T*>(c.A) + b0 * c.sA;
+        a.B = static_cast<const T*>(c.B) + b0 * c.sB;
+        a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
+        hipLaunchKernelGGL((bpt::gemm_generic_kernel<T, OutT>), dim3((unsigned)(tm * tn), (unsigned)nb),
+                           dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_zero(const Call& c, hipStream_t stream) {
+    long long total = c.M * c.N;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        hipLaunchKernelGGL((bpt::fill_zero_kernel<OutT>), dim3((unsigned)blocks, (unsigned)nb), dim3(256), 0,
+                           stream, static_cast<OutT*>(c.C) + b0 * c.sC, c.M, c.N, c.ldc, c.sC);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
+    if (c.K == 0) return launch_zero<OutT>(c, stream);
+    switch (v) {
+        case V_PIPE_256: return launch_pipelined<T, OutT, 256, 256>(c, stream);
+        case V_PIPE_128: return launch_pipelined<T, OutT, 128, 128>(c, stream);
+        default: return launch_generic<T, OutT>(c, stream);
+    }
+}
+
+bpt_status validate(const Call& c) {
+    if (c.dtype != 0 && c.dtype != 1) return fail(BPT_ERR_INVALID_ARG, "dtype must be 0 (fp16) or 1 (bf16), got %d", c.dtype);
+    if (c.out_fp32 != 0 && c.out_fp32 != 1) return fail(BPT_ERR_INVALID_ARG, "out_fp32 must be 0 or 1, got %d", c.out_fp32);
+    if (c.batch < 0 || c.M < 0 || c.N < 0 || c.K < 0)
+        return fail(BPT_ERR_INVALID_ARG, "negative size: batch=%lld M=%lld N=%lld K=%lld", c.batch, c.M, c.N, c.K);
+    if (c.lda < (c.K > 1 ? c.K : 1)) return fail(BPT_ERR_INVALID_ARG, "lda=%lld < max(1, K=%lld)", c.lda, c.K);
+    if (c.ldb < (c.N > 1 ? c.N : 1)) return fail(BPT_ERR_INVALID_ARG, "ldb=%lld < max(1, N=%lld)", c.ldb, c.N);
+    if (c.ldc < (c.N > 1 ? c.N : 1)) return fail(BPT_ERR_INVALID_ARG, "ldc=%lld < max(1, N=%lld)", c.ldc, c.N);
+    if (c.sA < 0 || c.sB < 0 || c.sC < 0)
+        return fail(BPT_ERR_INVALID_ARG, "negative batch stride: %lld %lld %lld", c.sA, c.sB, c.sC);
+    const bool nonempty = c.batch > 0 && c.M > 0 && c.N > 0;
+    if (nonempty) {
+        if (c.C == nullptr) return fail(BPT_ERR_INVALID_ARG, "C is NULL");
+        if (c.K > 0 && (c.A == nullptr || c.B == nullptr)) return fail(BPT_ERR_INVALID_ARG, "A or B is NULL");
+    }
+    if (c.M > kI31 || c.N > kI31 || c.K > kI31 || c.lda > kI31 || c.ldb > kI31 || c.ldc > kI31)
+        return fail(BPT_ERR_UNSUPPORTED, "a dimension or leading dimension exceeds 2^31-1");
+    return BPT_OK;
+}
+
+bool variant_accepts(const Call& c, int v) {
+    switch (v) {
+        case V_GENERIC: return true;
+        case V_PIPE_256:
+        case V_PIPE_128: return pipelined_ok(c, 64);
+        default: return false;
+    }
+}
+
+bpt_status run(const Call& c, int variant, hipStream_t stream) {
+    bpt_status s = validate(c);
+    if (s != BPT_OK) return s;
+    if (variant < 0 || variant > V_COUNT) return fail(BPT_ERR_INVALID_ARG, "no variant %d", variant);
+    if (c.batch == 0 || c.M == 0 || c.N == 0) return BPT_OK;
+    int v = variant == V_AUTO ? choose(c) : variant;
+    if (c.K > 0 && !variant_accepts(c, v))
+        return fail(BPT_ERR_UNSUPPORTED, "variant %s cannot take M=%lld N=%lld K=%lld lda=%lld ldb=%lld",
+                    kVariantNames[v], c.M, c.N, c.K, c.lda, c.ldb);
+    hipError_t e;
+    if (c.dtype == 0)
+        e = c.out_fp32 ? dispatch_typed<_Float16, float>(c, v, stream) : dispatch_typed<_Float16, _Float16>(c, v, stream);
+    else
+        e = c.out_fp32 ? dispatch_typed<__bf16, float>(c, v, stream) : dispatch_typed<__bf16, __bf16>(c, v, stream);
+    if (e != hipSuccess) return fail(BPT_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return BPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda, int64_t strideA,
+                   const void* B, int64_t ldb, int64_t strideB,
+                   void* C, int64_t ldc, int64_t strideC,
+                   int out_fp32, int variant, struct ihipStream_t* stream) {
+    Call c{dtype, batch, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, A, B, C, out_fp32};
+    return run(c, variant, reinterpret_cast<hipStream_t>(stream));
+}
+
+bpt_status gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    void* C, int64_t ldc, int out_fp32, struct ihipStream_t* stream) {
+    return gemm_ex(0, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, out_fp32, V_AUTO, stream);
+}
+
+bpt_status gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     void* C, int64_t ldc, int out_fp32, struct ihipStream_t* stream) {
+    return gemm_ex(1, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, out_fp32, V_AUTO, stream);
+}
+
+bpt_status gemm_batched_f16(int64_t batch, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, int64_t strideA,
+                            const void* B, int64_t ldb, int64_t strideB,
+                            void* C, int64_t ldc, int64_t strideC,
+                            int out_fp32, struct ihipStream_t* stream) {
+    return gemm_ex(0, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, out_fp32, V_AUTO, stream);
+}
+
+int bpt_select_variant(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, int out_fp32) {
+    Call c{dtype, batch, M, N, K, lda, ldb, N > 1 ? N : 1, 0, 0, 0, A, B, (void*)16, out_fp32};
+    if (validate(c) != BPT_OK) return 0;
+    if (batch == 0 || M == 0 || N == 0 || K == 0) return 0;
+    return choose(c);
+}
+
+int bpt_variant_count(void) { return V_COUNT; }
+
+const char* bpt_variant_name(int v) {
+    if (v < 1 || v > V_COUNT) return nullptr;
+    return kVariantNames[v];
+}
+
+const char* bpt_status_string(bpt_status s) {
+    switch (s) {
+        case BPT_OK: return "BPT_OK";
+        case BPT_ERR_INVALID_ARG: return "BPT_ERR_INVALID_ARG";
+        case BPT_ERR_UNSUPPORTED: return "BPT_ERR_UNSUPPORTED";
+        case BPT_ERR_HIP: return "BPT_ERR_HIP";
+    }
+    return "unknown status";
+}
+
+const char* bpt_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// device_common.hpp -- gfx950 (CDNA4) building blocks shared by the GEMM
+// kernels: vector types, buffer resource descriptors, LDS-DMA loads, the
+// explicit wait/barrier primitives and the MFMA wrappers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bpt {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+#define BPT_LDS __attribute__((address_space(3)))
+
+typedef int int4_t __attribute__((ext_vector_type(4)));
+
+// Word 3 of a gfx9-family raw buffer resource: 32-bit data format, no
+// swizzle, no stride, so num_records counts bytes and any access at or past
+// num_records returns zero instead of touching memory.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 128-bit buffer resource for `bytes` bytes starting at `base` (wave-uniform).
+__device__ inline int4_t make_rsrc(const void* base, uint32_t bytes) {
+    uint64_t p = reinterpret_cast<uint64_t>(base);
+    int4_t r;
+    r[0] = (int)(uint32_t)p;
+    r[1] = (int)((p >> 32) & 0xffff);     // stride 0, no swizzle
+    r[2] = (int)bytes;
+    r[3] = kBufferWord3;
+    return r;
+}
+
+// 32-bit LDS address of a pointer into LDS.
+__device__ inline uint32_t lds_addr(const BPT_LDS void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// One wave-wide 16-byte-per-lane global->LDS copy (LDS-DMA).  Lane p's 16
+// bytes come from rsrc.base + voff + soff and land at lds + 16*p, i.e. one
+// contiguous KiB per wave.  The copy is counted by this wave's vmcnt and has
+// reached LDS once vmcnt has dropped past it.
+//
+// Written as inline asm on purpose: the compiler cannot prove that a DMA
+// into one ring stage does not alias the reads of another stage, and for
+// the builtin form it inserts a vmcnt(0) before every later LDS read, which
+// serialises the pipeline.  Hidden from the compiler, these copies are
+// accounted for only by the explicit publish<>() waits below.
+__device__ inline void dma16(int4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Publish a ring stage: wait until at most N of this wave's copies are still
+// in flight (so the stage's copies of this wave have landed: the "bytes
+// pending" half of a stage-ready condition), wait for this wave's LDS reads,
+// then one s_barrier (the "all arrivals" half).  Every wave executes the same
+// sequence of publish calls.  The memory clobber keeps the compiler from
+// moving LDS reads across it.
+template <int N>
+__device__ inline void publish() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<_Float16> {
+    typedef half8_t frag_t;
+    __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<__bf16> {
+    typedef bf16x8_t frag_t;
+    __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Output conversions, round to nearest even.
+template <typename OutT>
+__device__ inline OutT cvt_out(float x);
+template <>
+__device__ inline float cvt_out<float>(float x) { return x; }
+template <>
+__device__ inline _Float16 cvt_out<_Float16>(float x) { return (_Float16)x; }
+template <>
+__device__ inline __bf16 cvt_out<__bf16>(float x) { return (__bf16)x; }
+
+}  // namespace bpt

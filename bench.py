@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the pipelined GEMM on one MI355X.
+
+Default workload: fp16 GEMM M = N = K = 4096 with fp16 output, 8 rotating
+(A, B, C) buffer sets so that consecutive calls do not hit each other's data
+in the caches; inputs uniform in [-1, 1) without zeros, seeded.  One "step"
+is one GEMM call (the whole hot path) on the next buffer set.
+
+Protocol (the "Xe2 ESIMD GEMM" page, "Performance testing" and "Workflow"):
+W untimed warm-up steps, a pause so the clocks settle, then exactly K timed
+steps between two device synchronisations.  The kernel time is measured with
+HIP events recorded on the stream the kernels are launched on.
+
+The JSON line also carries
+* roofline: algorithmic flops (or bytes, for the memory-bound shape) per
+  launch over the average launch duration, against MI355X's dense peak;
+* cpu_baseline: the CPU oracle timed on a bounded sample (leading rows of
+  the same product) on the host cores, scaled to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16_TFLOPS = 2516.6     # 256 CU x 2048 fp16 FMA/clk/CU x 2 x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "fp16 GEMM TFLOPS at M=N=K=4096 (1 MI355X); % of dense FP16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, A, B, budget_s: float = 12.0):
+    """Time the oracle on the first R rows of A times all of B (set 0)."""
+    import oracle
+    from barrier_pipelined_tiled_amd import inputs
+    a_bits = inputs.bits(A if A.dim() == 2 else A[0])
+    b_bits = inputs.bits(B if B.dim() == 2 else B[0])
+    K, N = b_bits.shape
+    rows = 8
+    t0 = time.perf_counter()
+    oracle.gemm(a_bits[:rows], b_bits, w.dtype)
+    t = time.perf_counter() - t0
+    rows = int(max(8, min(a_bits.shape[0], rows * budget_s / max(t, 1e-3))))
+    log(f"cpu_baseline: oracle on {rows} rows ...")
+    t0 = time.perf_counter()
+    oracle.gemm(a_bits[:rows], b_bits, w.dtype)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of A ({rows}x{K}) times B ({K}x{N}), "
+                  f"{w.dtype}, fp64 accumulation, {t:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="f16_4096")
+    ap.add_argument("--variant", type=int, default=0, help="0 = automatic choice")
+    ap.add_argument("--sleep", type=float, default=5.0, help="pause before timing (s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the GEMM of this library runs on a single "
+              "MI355X and has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import barrier_pipelined_tiled_amd as pkg
+    from barrier_pipelined_tiled_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    pkg.lib()
+    R = w.rotating
+    log(f"workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
+        f"out={'fp32' if w.out_fp32 else w.dtype} rotating={R}")
+
+    As, Bs, Cs = [], [], []
+    A0 = B0 = None
+    for j in range(R):
+        A = w.make_a(j) if (w.rotate_a or j == 0) else None
+        B = w.make_b(j)
+        if j == 0:
+            A0, B0 = A, B
+        As.append(A.to(dev) if A is not None else As[0])
+        Bs.append(B.to(dev))
+        out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
+        Cs.append(torch.empty(w.c_shape(), dtype=out_t, device=dev))
+    torch.cuda.synchronize()
+    log("inputs resident in HBM")
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % R
+        pkg.gemm_ex(As[j], Bs[j], Cs[j], dtype=w.dtype, out_fp32=w.out_fp32, variant=args.variant,
+                    stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.sleep > 0:
+        time.sleep(args.sleep)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (events)")
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    memory_bound = w.name.startswith("f16_skinny")
+    if memory_bound:
+        achieved = w.compulsory_bytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    else:
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None}
+
+    variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.N, w.out_fp32)
+    names = {v: k for k, v in pkg.variants().items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, A0, B0)
+
+    out = {
+        "metric": METRIC if w.name == "f16_4096" else f"{w.name} TFLOPS (1 MI355X)",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "f16" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+                   "in": w.dtype, "out": "fp32" if w.out_fp32 else w.dtype, "accumulate": "fp32",
+                   "rotating_buffers": R, "kernel": names.get(variant_id, str(variant_id)),
+                   "pct_of_dense_peak": 100.0 * value / PEAK_MFMA_F16_TFLOPS},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+/*
+ * bpt_gemm.h -- C ABI of the MI355X (gfx950) pipelined half-precision GEMM.
+ *
+ * Operation (every entry point): C <- A * B, overwriting C, with
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ * accumulated in fp32 on the matrix cores.  This is the tiled FP16 GEMM of
+ * the "Xe2 ESIMD GEMM" page (its B_T[K,N] layout: B is K rows of N, row
+ * major), rebuilt for CDNA4: K-tiles are staged global->LDS by LDS-DMA in a
+ * ring of stages, published to the workgroup by a vmcnt wait plus one
+ * s_barrier (the gfx950 form of the split arrive/wait barrier of the
+ * "Xe2 Nbarrier Pipelining" page), and consumed by v_mfma_f32_32x32x16.
+ * There is no alpha/beta.
+ *
+ * Layout: all matrices are row major.  A is M x K with leading dimension lda
+ * (elements between the starts of consecutive rows, lda >= max(1, K)); B is
+ * K x N with ldb >= max(1, N); C is M x N with ldc >= max(1, N).  Batch
+ * strides are in elements.
+ *
+ * Element types: gemm_f16 / gemm_batched_f16 read IEEE binary16, gemm_bf16
+ * reads bfloat16.  out_fp32 = 0 writes C in the input type (rounded to
+ * nearest even from the fp32 sum); out_fp32 = 1 writes fp32.
+ *
+ * Ownership: A, B and C are DEVICE pointers owned by the caller; the library
+ * allocates, frees and retains nothing per call and holds no per-call state.
+ * C must not overlap A or B.
+ *
+ * Execution: the call validates its arguments on the host, enqueues the
+ * kernel(s) on `stream` (NULL = the default stream) and returns without
+ * waiting.  Completion is observed by synchronising the stream.
+ *
+ * Errors: nothing is launched unless the status is BPT_OK.
+ *   BPT_ERR_INVALID_ARG  a size or stride is negative, a leading dimension is
+ *                        too small, out_fp32 is not 0/1, or a pointer of a
+ *                        non-empty operand is NULL;
+ *   BPT_ERR_UNSUPPORTED  a dimension or leading dimension does not fit in 31
+ *                        bits, or a forced variant cannot take the call;
+ *   BPT_ERR_HIP          the HIP runtime reported an error at launch.
+ * bpt_last_error() returns a message for the last failing call on the
+ * calling thread.
+ *
+ * Degenerate shapes: M == 0, N == 0 or batch == 0 returns BPT_OK and
+ * launches nothing; K == 0 writes zeros to C (the empty sum).
+ */
+#ifndef BPT_GEMM_H
+#define BPT_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t == struct ihipStream_t* */
+
+typedef enum {
+    BPT_OK = 0,
+    BPT_ERR_INVALID_ARG = 1,
+    BPT_ERR_UNSUPPORTED = 2,
+    BPT_ERR_HIP = 3
+} bpt_status;
+
+/* fp16 GEMM, C (M x N) = A (M x K) * B (K x N); C is fp16 or fp32. */
+bpt_status gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    void *C, int64_t ldc,
+                    int out_fp32, struct ihipStream_t *stream);
+
+/* bf16 GEMM; C is bf16 (out_fp32 = 0) or fp32 (out_fp32 = 1). */
+bpt_status gemm_bf16(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb,
+                     void *C, int64_t ldc,
+                     int out_fp32, struct ihipStream_t *stream);
+
+/* batch independent fp16 GEMMs; entry b uses A + b*strideA, B + b*strideB,
+ * C + b*strideC (strides in elements, >= 0). */
+bpt_status gemm_batched_f16(int64_t batch, int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda, int64_t strideA,
+                            const void *B, int64_t ldb, int64_t strideB,
+                            void *C, int64_t ldc, int64_t strideC,
+                            int out_fp32, struct ihipStream_t *stream);
+
+/* The general entry point behind the three above, with the kernel variant
+ * made explicit so that tests and benchmarks can pin one.
+ * dtype: 0 = fp16 inputs, 1 = bf16 inputs.  variant: 0 chooses
+ * automatically (what the three calls above do); 1 .. bpt_variant_count()
+ * forces that variant and returns BPT_ERR_UNSUPPORTED when its shape,
+ * alignment or type requirements are not met. */
+bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda, int64_t strideA,
+                   const void *B, int64_t ldb, int64_t strideB,
+                   void *C, int64_t ldc, int64_t strideC,
+                   int out_fp32, int variant, struct ihipStream_t *stream);
+
+/* Which variant gemm_ex(variant = 0) would run for these arguments (the
+ * pointers are only inspected for alignment).  Returns 0 when the call
+ * would be rejected or launch nothing. */
+int bpt_select_variant(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, const void *B, int64_t ldb,
+                       int out_fp32);
+
+/* Number of variants and the name of variant v (1-based); NULL if out of
+ * range.  Names spell the tile shape, K-tile and stage count. */
+int bpt_variant_count(void);
+const char *bpt_variant_name(int v);
+
+/* Static text for a status code. */
+const char *bpt_status_string(bpt_status s);
+
+/* Message of the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char *bpt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPT_GEMM_H */

@@ -1,0 +1,131 @@
+"""The C ABI: the library loads without a GPU, exports every function the
+header declares, and its host-side validation and variant choice behave as
+documented.  No kernel is launched here (every call below is rejected or is
+a no-op before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import barrier_pipelined_tiled_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpt_gemm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pkg.LIB_PATH):
+        from barrier_pipelined_tiled_amd import build
+        build.build()
+    return pkg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "bpt_status_string",
+              "bpt_last_error", "bpt_variant_count", "bpt_variant_name", "bpt_select_variant"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in bpt_gemm.h but not exported"
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "at::Tensor" not in text and "c10" not in text
+
+
+def test_status_strings(L):
+    assert L.bpt_status_string(0) == b"BPT_OK"
+    assert L.bpt_status_string(1) == b"BPT_ERR_INVALID_ARG"
+    assert L.bpt_status_string(2) == b"BPT_ERR_UNSUPPORTED"
+    assert L.bpt_status_string(3) == b"BPT_ERR_HIP"
+
+
+def test_variant_table(L):
+    names = pkg.variants()
+    assert len(names) == L.bpt_variant_count() >= 3
+    assert L.bpt_variant_name(0) is None and L.bpt_variant_name(L.bpt_variant_count() + 1) is None
+    assert "generic_64x64x16" in names
+    assert any(n.startswith("pipelined_256x256x64") for n in names)
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced below
+
+
+@pytest.mark.parametrize("args,what", [
+    ((-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0), "negative M"),
+    ((4, -1, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0), "negative N"),
+    ((4, 4, -1, FAKE, 4, FAKE, 4, FAKE, 4, 0), "negative K"),
+    ((4, 4, 8, FAKE, 7, FAKE, 4, FAKE, 4, 0), "lda < K"),
+    ((4, 8, 4, FAKE, 4, FAKE, 7, FAKE, 8, 0), "ldb < N"),
+    ((4, 8, 4, FAKE, 4, FAKE, 8, FAKE, 7, 0), "ldc < N"),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 2), "out_fp32 not 0/1"),
+    ((4, 4, 4, 0, 4, FAKE, 4, FAKE, 4, 0), "A NULL"),
+    ((4, 4, 4, FAKE, 4, 0, 4, FAKE, 4, 0), "B NULL"),
+    ((4, 4, 4, FAKE, 4, FAKE, 4, 0, 4, 0), "C NULL"),
+])
+def test_invalid_arguments_rejected(L, args, what):
+    for fn in (L.gemm_f16, L.gemm_bf16):
+        st = fn(*args, None)
+        assert st == pkg.BPT_ERR_INVALID_ARG, what
+        assert L.bpt_last_error().decode() != ""
+
+
+def test_batched_invalid(L):
+    st = L.gemm_batched_f16(-1, 4, 4, 4, FAKE, 4, 16, FAKE, 4, 16, FAKE, 4, 16, 0, None)
+    assert st == pkg.BPT_ERR_INVALID_ARG
+    st = L.gemm_batched_f16(2, 4, 4, 4, FAKE, 4, -16, FAKE, 4, 16, FAKE, 4, 16, 0, None)
+    assert st == pkg.BPT_ERR_INVALID_ARG
+    st = L.gemm_ex(2, 1, 4, 4, 4, FAKE, 4, 0, FAKE, 4, 0, FAKE, 4, 0, 0, 0, None)
+    assert st == pkg.BPT_ERR_INVALID_ARG          # dtype 2 does not exist
+    st = L.gemm_ex(0, 1, 4, 4, 4, FAKE, 4, 0, FAKE, 4, 0, FAKE, 4, 0, 0, 99, None)
+    assert st == pkg.BPT_ERR_INVALID_ARG          # no variant 99
+
+
+def test_oversized_dimension_unsupported(L):
+    big = 1 << 31
+    st = L.gemm_f16(4, big, 4, FAKE, 4, FAKE, big, FAKE, big, 0, None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+
+
+def test_empty_shapes_are_noops(L):
+    # nothing to compute: OK with no launch (NULL pointers allowed)
+    assert L.gemm_f16(0, 16, 16, 0, 16, 0, 16, 0, 16, 0, None) == pkg.BPT_OK
+    assert L.gemm_f16(16, 0, 16, 0, 16, 0, 1, 0, 1, 0, None) == pkg.BPT_OK
+    assert L.gemm_batched_f16(0, 16, 16, 16, 0, 16, 0, 0, 16, 0, 0, 16, 0, 0, None) == pkg.BPT_OK
+
+
+def test_forced_variant_that_cannot_take_the_call(L):
+    v = pkg.variants()["pipelined_256x256x64_s2"]
+    # K = 100 is not a multiple of the 64-wide K-tile
+    st = L.gemm_ex(0, 1, 256, 256, 100, FAKE, 100, 0, FAKE, 256, 0, FAKE, 256, 0, 0, v, None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+    # unaligned A
+    st = L.gemm_ex(0, 1, 256, 256, 128, FAKE + 2, 128, 0, FAKE, 256, 0, FAKE, 256, 0, 0, v, None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+
+
+def test_automatic_variant_choice():
+    v = pkg.variants()
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == v["pipelined_256x256x64_s2"]
+    assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == v["pipelined_256x256x64_s2"]
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == v["pipelined_256x256x64_s2"]
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256) == v["pipelined_128x128x64_s2"]
+    # K not a multiple of 64, odd leading dimension, unaligned base: generic
+    assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["generic_64x64x16"]
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == v["generic_64x64x16"]
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == v["generic_64x64x16"]
+    # rejected / nothing to do
+    assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0
+    assert pkg.select_variant("f16", 1, 16, 16, 16, 8, 16) == 0

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP kernels (called through the C ABI) against the CPU
+oracle on the same seeded inputs.
+
+* random inputs: rel-RMS <= 5e-3 and max|err| <= 2e-2 sqrt(K/256) max|C_ref|
+  after a non-finite check (the oracle's ``compare``);
+* small-integer inputs: every partial sum is an exact integer in fp32, so any
+  summation order gives the same fp32 result -- the GPU must match the
+  oracle bit for bit (fp32 output) or match the oracle's round-to-nearest-
+  even 16-bit encoding of it bit for bit (16-bit output);
+* full workload sizes run the automatic choice (what the benchmark times)
+  and compare sampled outputs computed one by one by the oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import barrier_pipelined_tiled_amd as pkg
+import oracle
+from barrier_pipelined_tiled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkg.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run(A, B, dtype="f16", out_fp32=False, variant=0, C=None):
+    """GEMM of CPU tensors on the GPU; returns the CPU result."""
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    Cd = pkg.gemm_ex(Ad, Bd, C, dtype=dtype, out_fp32=out_fp32, variant=variant)
+    torch.cuda.synchronize()
+    return Cd.cpu()
+
+
+def as_bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_random(A, B, dtype, out_fp32, variant=0):
+    got = run(A, B, dtype, out_fp32, variant)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B), dtype)
+    m = oracle.compare(got.float().numpy(), ref, A.shape[-1])
+    assert m["ok"], m
+    return m
+
+
+def check_exact(A, B, dtype, out_fp32, variant=0):
+    got = run(A, B, dtype, out_fp32, variant)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B), dtype)
+    if out_fp32:
+        assert np.array_equal(got.numpy(), ref)
+    else:
+        assert np.array_equal(as_bits(got), oracle.encode(ref, dtype))
+
+
+VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2"]
+# the pipelined variants need K % 64 == 0 and 16-byte aligned rows (ld % 8 == 0);
+# M is free, and a ragged N is exercised with a padded ldb below
+SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 128), (1, 8, 64), (33, 520, 192),
+               (129, 136, 64), (640, 768, 512)]
+SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64)]
+
+
+def _shapes(vname):
+    return SHAPES_PIPE + (SHAPES_GENERIC_ONLY if vname.startswith("generic") else [])
+
+
+@pytest.mark.parametrize("vname", VARIANTS)
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True), ("bf16", False)])
+def test_variant_parity_random(vname, dtype, out_fp32):
+    v = pkg.variants()[vname]
+    for i, (M, N, K) in enumerate(_shapes(vname)):
+        say(f"[random] {vname} {dtype} out_fp32={out_fp32} M={M} N={N} K={K}")
+        A = inputs.uniform((M, K), 1000 + i, dtype=dtype, nonzero=True)
+        B = inputs.uniform((K, N), 2000 + i, dtype=dtype, nonzero=True)
+        check_random(A, B, dtype, out_fp32, v)
+
+
+@pytest.mark.parametrize("vname", VARIANTS)
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True)])
+def test_variant_parity_exact_integers(vname, dtype, out_fp32):
+    v = pkg.variants()[vname]
+    for i, (M, N, K) in enumerate(_shapes(vname)):
+        say(f"[exact] {vname} {dtype} out_fp32={out_fp32} M={M} N={N} K={K}")
+        A = inputs.small_integers((M, K), 3000 + i, dtype=dtype)
+        B = inputs.small_integers((K, N), 4000 + i, dtype=dtype)
+        check_exact(A, B, dtype, out_fp32, v)
+
+
+def test_small_workload_all_rotating_sets():
+    w = inputs.WORKLOADS["f16_256"]
+    for j in range(w.rotating):
+        say(f"[f16_256] set {j}")
+        A, B = w.make_a(j), w.make_b(j)
+        m = check_random(A, B, "f16", False)
+        assert m["rel_rms"] < 1e-3
+
+
+def test_identity_and_permutation_exact():
+    K = 512
+    B = inputs.uniform((K, 384), 5001, nonzero=True)
+    I = torch.eye(K, dtype=torch.float16)
+    assert torch.equal(run(I, B), B)                       # A = I gives B exactly
+    perm = torch.randperm(K, generator=torch.Generator().manual_seed(5))
+    P = torch.zeros(K, K, dtype=torch.float16)
+    P[torch.arange(K), perm] = 1
+    assert torch.equal(run(P, B), B[perm])                 # P B permutes rows
+
+
+def test_padded_leading_dimensions_nan_padding():
+    """lda > K, ldb > N, ldc > N with NaN in every padding element: the
+    result must be finite and correct, and C's padding must be untouched.
+    N = 201 is not a multiple of 8: the last column chunk of B straddles N."""
+    M, N, K = 300, 201, 192
+    for vname in VARIANTS:
+        v = pkg.variants()[vname]
+        say(f"[padded] {vname}")
+        A = inputs.uniform((M, K), 6001, nonzero=True)
+        B = inputs.uniform((K, N), 6002, nonzero=True)
+        Ap = torch.full((M, K + 8), float("nan"), dtype=torch.float16)
+        Ap[:, :K] = A
+        Bp = torch.full((K, N + 23), float("nan"), dtype=torch.float16)
+        Bp[:, :N] = B
+        Cp = torch.full((M, N + 8), 7.0, dtype=torch.float16, device=DEV)
+        pkg.gemm_ex(Ap.to(DEV)[:, :K], Bp.to(DEV)[:, :N], Cp[:, :N], variant=v)
+        torch.cuda.synchronize()
+        Cp = Cp.cpu()
+        assert torch.all(Cp[:, N:] == 7.0)
+        ref = oracle.gemm(inputs.bits(A), inputs.bits(B))
+        m = oracle.compare(Cp[:, :N].float().numpy(), ref, K)
+        assert m["ok"], (vname, m)
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop():
+    C = torch.full((40, 24), 3.0, dtype=torch.float16, device=DEV)
+    A = torch.empty((40, 0), dtype=torch.float16, device=DEV)
+    B = torch.empty((0, 24), dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(A, B, C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+    C2 = torch.full((0, 24), 3.0, dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(torch.empty((0, 8), dtype=torch.float16, device=DEV),
+                torch.ones((8, 24), dtype=torch.float16, device=DEV), C2)
+
+
+@pytest.mark.parametrize("vname", VARIANTS)
+def test_batched_small(vname):
+    v = pkg.variants()[vname]
+    b, M, N, K = 3, 160, 192, 128
+    say(f"[batched] {vname}")
+    A = inputs.uniform((b, M, K), 7001, lo=-0.5, hi=0.5)
+    B = inputs.uniform((b, K, N), 7002, lo=-0.5, hi=0.5)
+    got = run(A, B, "f16", False, v)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B))
+    m = oracle.compare(got.float().numpy(), ref, K)
+    assert m["ok"], m
+    Ai = inputs.small_integers((b, M, K), 7003)
+    Bi = inputs.small_integers((b, K, N), 7004)
+    gi = run(Ai, Bi, "f16", True, v)
+    assert np.array_equal(gi.numpy(), oracle.gemm(inputs.bits(Ai), inputs.bits(Bi)))
+
+
+def test_batched_entry_point():
+    b, M, N, K = 4, 256, 256, 256
+    A = inputs.uniform((b, M, K), 7101, lo=-0.5, hi=0.5)
+    B = inputs.uniform((b, K, N), 7102, lo=-0.5, hi=0.5)
+    C = pkg.gemm_batched_f16(A.to(DEV), B.to(DEV))
+    torch.cuda.synchronize()
+    m = oracle.compare(C.cpu().float().numpy(), oracle.gemm(inputs.bits(A), inputs.bits(B)), K)
+    assert m["ok"], m
+
+
+def test_repeat_runs_bitwise_identical():
+    w = inputs.WORKLOADS["f16_256"]
+    A, B = w.make_a(0).to(DEV), w.make_b(0).to(DEV)
+    outs = [pkg.gemm_f16(A, B).cpu() for _ in range(5)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, automatic variant choice (the benchmark's launches)
+# ----------------------------------------------------------------------------
+
+def _sample_positions(batch, M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    b = rng.integers(0, batch, n)
+    r = rng.integers(0, M, n)
+    c = rng.integers(0, N, n)
+    # corners of the first and last batch entry
+    b = np.concatenate([b, [0, 0, batch - 1, batch - 1]])
+    r = np.concatenate([r, [0, M - 1, 0, M - 1]])
+    c = np.concatenate([c, [N - 1, 0, 0, N - 1]])
+    return b, r, c
+
+
+def _full_size(w, A, B):
+    """Run workload w on the GPU; return (all-finite flag, sampled GPU values
+    as float64, sample positions)."""
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    if w.batch > 1:
+        C = pkg.gemm_batched_f16(Ad, Bd, out_fp32=w.out_fp32)
+    elif w.dtype == "f16":
+        C = pkg.gemm_f16(Ad, Bd, out_fp32=w.out_fp32)
+    else:
+        C = pkg.gemm_bf16(Ad, Bd, out_fp32=w.out_fp32)
+    torch.cuda.synchronize()
+    finite = bool(torch.isfinite(C).all().item())
+    C3 = C if C.dim() == 3 else C.unsqueeze(0)
+    b, r, c = _sample_positions(w.batch, w.M, w.N, 4096, 17)
+    idx = torch.from_numpy(np.stack([b, r, c])).to(DEV)
+    vals = C3[idx[0], idx[1], idx[2]]
+    return finite, vals, (b, r, c)
+
+
+FULL = ["f16_4096", "bf16_4096x4096x16384", "f16_batched_64x4096x4096x256", "f16_skinny_64x8192x8192"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = inputs.WORKLOADS[name]
+    say(f"[full] {name}")
+    A, B = w.make_a(0), w.make_b(0)
+    assert pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.N, w.out_fp32) != \
+        pkg.variants()["generic_64x64x16"]
+    finite, vals, (b, r, c) = _full_size(w, A, B)
+    assert finite, "non-finite values in the output"
+    ref = oracle.gemm_at(inputs.bits(A), inputs.bits(B), b, r, c, w.dtype)
+    m = oracle.compare(vals.float().cpu().numpy(), ref, w.K)
+    say(f"[full] {name} rel_rms={m['rel_rms']:.3e} max_abs={m['max_abs']:.3e}")
+    assert m["ok"], m
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_exact_integers(name):
+    """Integer inputs in [-2, 2] at the full shape: sampled outputs must match
+    the oracle bit for bit (|C| <= 4K stays inside fp16 for K <= 8192)."""
+    w = inputs.WORKLOADS[name]
+    say(f"[full-exact] {name}")
+    A = inputs.small_integers(w.a_shape(), 8001, dtype=w.dtype)
+    B = inputs.small_integers(w.b_shape(), 8002, dtype=w.dtype)
+    finite, vals, (b, r, c) = _full_size(w, A, B)
+    assert finite
+    ref = oracle.gemm_at(inputs.bits(A), inputs.bits(B), b, r, c, w.dtype)
+    got = vals.cpu()
+    if w.out_fp32:
+        assert np.array_equal(got.numpy(), ref)
+    else:
+        assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
