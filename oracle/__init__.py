@@ -179,8 +179,13 @@ REL_RMS_TOL = 5e-3
 
 
 def max_abs_tol(K: int, ref_absmax: float) -> float:
-    """Element-wise bound 2e-2 * sqrt(K/256) * max|C_ref|."""
-    return 2e-2 * np.sqrt(max(K, 1) / 256.0) * ref_absmax
+    """Element-wise bound 2e-2 * sqrt(max(K, 256)/256) * max|C_ref|.
+
+    The sqrt(K/256) growth is measured from the 256-wide correctness shape;
+    for K < 256 the K = 256 bound applies, since a shorter sum accumulates
+    no more error and the bound must still admit the output rounding of a
+    16-bit result (half an ulp of bf16 is 2^-9 of the value)."""
+    return 2e-2 * np.sqrt(max(K, 256) / 256.0) * ref_absmax
 
 
 def compare(gpu: np.ndarray, ref: np.ndarray, K: int) -> dict:

@@ -345,8 +345,13 @@ def test_metrics_hand_computed():
     zz = z.copy()
     zz[0, 0] = 1e-30
     assert not oracle.compare(zz, z, K=0)["ok"]
-    # max-abs bound scales with sqrt(K / 256)
+    # max-abs bound scales with sqrt(K / 256) from K = 256 up
     assert abs(oracle.max_abs_tol(1024, 1.0) - 4e-2) < 1e-15
+    assert oracle.max_abs_tol(1, 1.0) == oracle.max_abs_tol(256, 1.0) == 2e-2
+    # a K = 1 product rounded to bf16 (relative error up to 2^-9) passes
+    r = np.array([[1.0 + 2.0 ** -8]])
+    g = np.array([[1.0]])
+    assert oracle.compare(g, r, K=1)["ok"]
 
 
 # ----------------------------------------------------------------------------
