@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
@@ -45,7 +45,7 @@ def device_asm(out_dir: str) -> str:
     """Emit the gfx950 assembly of the library into out_dir; returns the .s path."""
     os.makedirs(out_dir, exist_ok=True)
     s_path = os.path.join(out_dir, "api-gfx950.s")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "--cuda-device-only", "-S", "-o", s_path, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -56,9 +56,10 @@ constexpr long long kI31 = (1LL << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Can a pipelined variant with tile (BM, BN, BK) take this call?
-bool pipelined_ok(const Call& c, int BK) {
-    if (c.K <= 0 || c.K % BK != 0) return false;
+// Can a pipelined variant with K-tile BK and STAGES ring stages take this
+// call?  The prologue fills every stage, so K must span at least STAGES tiles.
+bool pipelined_ok(const Call& c, int BK, int STAGES) {
+    if (c.K <= 0 || c.K % BK != 0 || c.K / BK < STAGES) return false;
     if (!aligned16(c.A) || !aligned16(c.B)) return false;
     if (c.lda % 8 != 0 || c.ldb % 8 != 0) return false;
     if (c.sA % 8 != 0 || c.sB % 8 != 0) return false;
@@ -71,7 +72,7 @@ bool pipelined_ok(const Call& c, int BK) {
 }
 
 int choose(const Call& c) {
-    if (!pipelined_ok(c, 64)) return V_GENERIC;
+    if (!pipelined_ok(c, 64, 2)) return V_GENERIC;
     long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     return tiles256 >= 128 ? V_PIPE_256 : V_PIPE_128;
 }
@@ -163,7 +164,7 @@ bool variant_accepts(const Call& c, int v) {
     switch (v) {
         case V_GENERIC: return true;
         case V_PIPE_256:
-        case V_PIPE_128: return pipelined_ok(c, 64);
+        case V_PIPE_128: return pipelined_ok(c, 64, 2);
         default: return false;
     }
 }

@@ -33,6 +33,8 @@
 // (BM/WM) x (BN/WN) built from 32x32 MFMA blocks (v_mfma_f32_32x32x16).
 // STAGES LDS buffers of (BM + BN) * BK halves each form the staging ring.
 #pragma once
+#include <utility>
+
 #include "device_common.hpp"
 
 namespace bpt {
@@ -119,6 +121,7 @@ struct PipelinedGemm {
     static constexpr int B_CHUNKS = BN / 8;
     static_assert(A_INST % 4 == 0 && B_INST % 4 == 0, "stage must split evenly over 4 waves");
     static_assert(LOADS_PER_STAGE * (STAGES - 1) < 64, "vmcnt is 6 bits");
+    static_assert(KS % 2 == 0, "fragment double-buffering alternates sets per k-step");
 
     typedef typename Mfma<T>::frag_t frag_t;
 };
@@ -193,16 +196,20 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
 
     BPT_LDS char* lds_bytes = (BPT_LDS char*)lds;
 
-    // LDS byte address of this wave's first DMA slot in stage 0 (uniform)
+    // LDS byte address of the ring (uniform)
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_bytes));
-    auto issue_stage = [&](int stage, uint32_t kA, uint32_t kB) {
-        const uint32_t sbase = lds0 + stage * (G::STAGE * 2);
-#pragma unroll
-        for (int i = 0; i < G::A_INST_W; ++i)
+    constexpr int STAGE_BYTES = G::STAGE * 2;
+    constexpr int LPS = G::LOADS_PER_STAGE;
+
+    // copy number i (0 .. LPS-1) of this wave for the tile at k offsets
+    // (kA, kB) into ring stage `stage`: A instructions first, then B
+    auto dma_one = [&](int stage, int i, uint32_t kA, uint32_t kB) {
+        const uint32_t sbase = lds0 + stage * STAGE_BYTES;
+        if (i < G::A_INST_W)
             dma16(rsA, sbase + (wave * G::A_INST_W + i) * 1024, voffA[i], kA);
-#pragma unroll
-        for (int i = 0; i < G::B_INST_W; ++i)
-            dma16(rsB, sbase + G::A_STAGE * 2 + (wave * G::B_INST_W + i) * 1024, voffB[i], kB);
+        else
+            dma16(rsB, sbase + G::A_STAGE * 2 + (wave * G::B_INST_W + (i - G::A_INST_W)) * 1024,
+                  voffB[i - G::A_INST_W], kB);
     };
 
     float16_t acc[G::MB][G::NB];
@@ -213,61 +220,108 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
             acc[i][j] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                                   0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    auto compute_stage = [&](int stage) {
-        BPT_LDS char* sbase = lds_bytes + stage * (G::STAGE * 2);
+    // Operand fragments of one MFMA k-step, double-buffered in registers.
+    frag_t fa0[G::MB], fb0[G::NB], fa1[G::MB], fb1[G::NB];
+
+    auto load_frags = [&](int stage, int ks, frag_t (&a)[G::MB], frag_t (&b)[G::NB]) {
+        BPT_LDS char* sbase = lds_bytes + stage * STAGE_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            frag_t a[G::MB], b[G::NB];
+        for (int mb = 0; mb < G::MB; ++mb)
+            a[mb] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + mb * 32 * BK * 2);
 #pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb)
-                a[mb] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + mb * 32 * BK * 2);
+        for (int nb = 0; nb < G::NB; ++nb) {
+            BPT_LDS char* p = sbase + rdB[nb] + ks * 16 * BN * 2;
+            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
+            b[nb] = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    // All MFMAs of one k-step; when `with_dma`, the next-next tile's copies
+    // are issued between them (ceil(LPS / MFMAs) per MFMA).
+    constexpr int NMMA = G::MB * G::NB;
+    constexpr int DMA_PER_MMA = (LPS + NMMA - 1) / NMMA;
+    auto mma_step = [&](frag_t (&a)[G::MB], frag_t (&b)[G::NB], bool with_dma, int stage,
+                        uint32_t kA, uint32_t kB) {
 #pragma unroll
-            for (int nb = 0; nb < G::NB; ++nb) {
-                BPT_LDS char* p = sbase + rdB[nb] + ks * 16 * BN * 2;
-                short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
-                short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
-                short8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                b[nb] = __builtin_bit_cast(frag_t, both);
+        for (int q = 0; q < NMMA; ++q) {
+            const int mb = q / G::NB, nb = q % G::NB;
+            acc[mb][nb] = Mfma<T>::mma32(a[mb], b[nb], acc[mb][nb]);
+            if (with_dma) {
+#pragma unroll
+                for (int r = 0; r < DMA_PER_MMA; ++r)
+                    if (q * DMA_PER_MMA + r < LPS) dma_one(stage, q * DMA_PER_MMA + r, kA, kB);
+                __builtin_amdgcn_sched_barrier(0);     // keep copies spread between MFMAs
             }
-#pragma unroll
-            for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < G::NB; ++nb)
-                    acc[mb][nb] = Mfma<T>::mma32(a[mb], b[nb], acc[mb][nb]);
         }
     };
 
     // ---- a4/a5: prologue, steady state, drain --------------------------------
-    const int nk = K / BK;                 // host guarantees K % BK == 0, nk >= STAGES-1
-    uint32_t kA = 0, kB = 0;
+    //
+    // Tile j lives in ring stage j % STAGES.  Per tile, k-steps 0 .. KS-2 read
+    // the next k-step's fragments while the MFMAs of the current one run.
+    // Then comes the publish point of tile j+1 and its window:
+    //   publish(j+1): own copies of tile j+1 landed + s_barrier.  Every wave
+    //                 has also finished its reads of tile j's stage.
+    //   window:       read tile j+1's first fragments, then run tile j's last
+    //                 k-step from registers while issuing the copies of tile
+    //                 j+STAGES into the stage tile j just vacated.
+    // The copies of a tile are in flight for STAGES-1 full tiles of MFMA work.
+    const int nk = K / BK;                 // host guarantees K % BK == 0 and nk >= STAGES
+    uint32_t kA = 0, kB = 0;               // byte offsets of the next tile to copy
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) {
-        issue_stage(s, kA, kB);
+    for (int s = 0; s < STAGES; ++s) {
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) dma_one(s, i, kA, kB);
         kA += a_step;
         kB += b_step;
     }
-    int stage_c = 0;                       // stage consumed this iteration
-    int stage_l = STAGES - 1;              // stage loaded this iteration
-    for (int t = 0; t < nk - (STAGES - 1); ++t) {
-        // own copies of tile t landed, then all waves': stage_c is published and
-        // every wave is done reading stage_l (consumed one iteration ago)
-        publish<G::LOADS_PER_STAGE * (STAGES - 2)>();
-        issue_stage(stage_l, kA, kB);                     // window: next tile's copies
-        kA += a_step;
-        kB += b_step;
-        compute_stage(stage_c);
-        stage_c = (stage_c + 1 == STAGES) ? 0 : stage_c + 1;
-        stage_l = (stage_l + 1 == STAGES) ? 0 : stage_l + 1;
-    }
-    // drain: the last STAGES-1 tiles, no new copies; wait counts fall to zero
+    publish<LPS * (STAGES - 1)>();         // tile 0 is in LDS for every wave
+    load_frags(0, 0, fa0, fb0);
+    int sc = 0;                            // stage of the tile being consumed
+
+    // one tile; DMA: issue tile j+STAGES in the window; VM: vmcnt for
+    // publish(j+1); LAST: final tile (no publish, no next reads)
+    auto tile = [&]<bool DMA, int VM, bool LAST>() {
 #pragma unroll
-    for (int d = 0; d < STAGES - 1; ++d) {
-        if (d == 0) publish<G::LOADS_PER_STAGE * (STAGES - 2)>();
-        else if (d == 1) publish<(STAGES >= 3) ? G::LOADS_PER_STAGE * (STAGES - 3) : 0>();
-        else publish<(STAGES >= 4) ? G::LOADS_PER_STAGE * (STAGES - 4) : 0>();
-        compute_stage(stage_c);
-        stage_c = (stage_c + 1 == STAGES) ? 0 : stage_c + 1;
-    }
+        for (int ks = 0; ks < G::KS - 1; ++ks) {
+            // the next k-step's reads are issued before this k-step's MFMAs
+            // (the fence stops the scheduler from sinking them to their use)
+            if (ks % 2 == 0) {
+                load_frags(sc, ks + 1, fa1, fb1);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_step(fa0, fb0, false, 0, 0, 0);
+            } else {
+                load_frags(sc, ks + 1, fa0, fb0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma_step(fa1, fb1, false, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (!LAST) {
+            publish<VM>();
+            const int sn = (sc + 1 == STAGES) ? 0 : sc + 1;
+            load_frags(sn, 0, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_step(fa1, fb1, DMA, sc, kA, kB);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DMA) {
+                kA += a_step;
+                kB += b_step;
+            }
+            sc = sn;
+        } else {
+            mma_step(fa1, fb1, false, 0, 0, 0);
+        }
+    };
+
+    for (int j = 0; j < nk - STAGES; ++j) tile.template operator()<true, LPS * (STAGES - 2), false>();
+    // drain: the last STAGES tiles issue no copies; the wait counts fall to 0
+    [&]<int... D>(std::integer_sequence<int, D...>) {
+        ((D < STAGES - 1 ? tile.template operator()<false, LPS * (STAGES - 2 - (D < STAGES - 1 ? D : 0)), false>()
+                         : tile.template operator()<false, 0, true>()),
+         ...);
+    }(std::make_integer_sequence<int, STAGES>{});
 
     // ---- a8: epilogue ---------------------------------------------------------
     // 32x32 block result layout: lane l, register r holds

@@ -126,6 +126,8 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == v["generic_64x64x16"]
+    # K = 64 is one K-tile, fewer than the two ring stages
+    assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
     # rejected / nothing to do
     assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0
     assert pkg.select_variant("f16", 1, 16, 16, 16, 8, 16) == 0

@@ -65,11 +65,12 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2"]
-# the pipelined variants need K % 64 == 0 and 16-byte aligned rows (ld % 8 == 0);
-# M is free, and a ragged N is exercised with a padded ldb below
-SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 128), (1, 8, 64), (33, 520, 192),
-               (129, 136, 64), (640, 768, 512)]
-SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64)]
+# the pipelined variants need K % 64 == 0, K >= 128 (two ring stages) and
+# 16-byte aligned rows (ld % 8 == 0); M is free, and a ragged N is exercised
+# with a padded ldb below
+SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 128), (1, 8, 128), (33, 520, 192),
+               (129, 136, 128), (640, 768, 512), (256, 512, 1024)]
+SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64)]
 
 
 def _shapes(vname):
