@@ -31,9 +31,12 @@ bpt_status fail(bpt_status s, const char* fmt, ...) {
 enum Variant {
     V_AUTO = 0,
     V_GENERIC = 1,          // guarded 64x64, any shape / alignment
-    V_PIPE_256 = 2,         // 256x256 tile, BK 64, 2 stages
-    V_PIPE_128 = 3,         // 128x128 tile, BK 64, 2 stages
-    V_COUNT = 3
+    V_PIPE_256_K64_S2 = 2,  // 256x256 tile, BK 64, 2 stages
+    V_PIPE_128_K64_S2 = 3,  // 128x128 tile, BK 64, 2 stages
+    V_PIPE_256_K32_S4 = 4,  // 256x256 tile, BK 32, 4 stages
+    V_PIPE_256_K32_S5 = 5,  // 256x256 tile, BK 32, 5 stages
+    V_PIPE_128_K32_S4 = 6,  // 128x128 tile, BK 32, 4 stages
+    V_COUNT = 6
 };
 
 const char* const kVariantNames[] = {
@@ -41,7 +44,14 @@ const char* const kVariantNames[] = {
     "generic_64x64x16",
     "pipelined_256x256x64_s2",
     "pipelined_128x128x64_s2",
+    "pipelined_256x256x32_s4",
+    "pipelined_256x256x32_s5",
+    "pipelined_128x128x32_s4",
 };
+
+// K-tile and stage count of each pipelined variant (0 for the others)
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4};
 
 struct Call {
     int dtype;
@@ -72,12 +82,16 @@ bool pipelined_ok(const Call& c, int BK, int STAGES) {
 }
 
 int choose(const Call& c) {
-    if (!pipelined_ok(c, 64, 2)) return V_GENERIC;
     long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
-    return tiles256 >= 128 ? V_PIPE_256 : V_PIPE_128;
+    const bool big = tiles256 >= 128;
+    if (big && pipelined_ok(c, 32, 4)) return V_PIPE_256_K32_S4;
+    if (pipelined_ok(c, 32, 4)) return V_PIPE_128_K32_S4;
+    if (big && pipelined_ok(c, 64, 2)) return V_PIPE_256_K64_S2;
+    if (pipelined_ok(c, 64, 2)) return V_PIPE_128_K64_S2;
+    return V_GENERIC;
 }
 
-template <typename T, typename OutT, int BM, int BN>
+template <typename T, typename OutT, int BM, int BN, int BK, int STAGES>
 hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
     bpt::GemmArgs a;
     a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
@@ -86,13 +100,15 @@ hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
     a.tiles_m = (int)((c.M + BM - 1) / BM);
     a.tiles_n = (int)((c.N + BN - 1) / BN);
     a.group_m = 4;
+    const long long ob = (long long)sizeof(OutT);
+    a.c_vec = aligned16(c.C) && (c.ldc * ob) % 16 == 0 && (c.sC * ob) % 16 == 0;
     const long long tiles = (long long)a.tiles_m * a.tiles_n;
     for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
         long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;
         a.B = static_cast<const T*>(c.B) + b0 * c.sB;
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
-        hipLaunchKernelGGL((bpt::gemm_pipelined_kernel<T, BM, BN, 64, 2, 2, 2, OutT>),
+        hipLaunchKernelGGL((bpt::gemm_pipelined_kernel<T, BM, BN, BK, STAGES, 2, 2, OutT>),
                            dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
@@ -134,8 +150,11 @@ template <typename T, typename OutT>
 hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
     if (c.K == 0) return launch_zero<OutT>(c, stream);
     switch (v) {
-        case V_PIPE_256: return launch_pipelined<T, OutT, 256, 256>(c, stream);
-        case V_PIPE_128: return launch_pipelined<T, OutT, 128, 128>(c, stream);
+        case V_PIPE_256_K64_S2: return launch_pipelined<T, OutT, 256, 256, 64, 2>(c, stream);
+        case V_PIPE_128_K64_S2: return launch_pipelined<T, OutT, 128, 128, 64, 2>(c, stream);
+        case V_PIPE_256_K32_S4: return launch_pipelined<T, OutT, 256, 256, 32, 4>(c, stream);
+        case V_PIPE_256_K32_S5: return launch_pipelined<T, OutT, 256, 256, 32, 5>(c, stream);
+        case V_PIPE_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4>(c, stream);
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -163,9 +182,9 @@ bpt_status validate(const Call& c) {
 bool variant_accepts(const Call& c, int v) {
     switch (v) {
         case V_GENERIC: return true;
-        case V_PIPE_256:
-        case V_PIPE_128: return pipelined_ok(c, 64, 2);
-        default: return false;
+        default:
+            if (v > V_GENERIC && v <= V_COUNT) return pipelined_ok(c, kVariantBK[v], kVariantStages[v]);
+            return false;
     }
 }
 

@@ -15,19 +15,23 @@
 //   only s_barrier and the per-wave vmcnt.  So each K-tile's LDS stage is
 //   published by two steps: (1) the wave waits until its own LDS-DMA copies
 //   for that stage have landed (s_waitcnt vmcnt(n), the tx-count half), then
-//   (2) one s_barrier (the arrival half).  The "window" between publish and
-//   consume holds the issue of the next stage's global->LDS copies, which
-//   then fly during the whole MFMA phase of the current stage.
-// * The same page, "What Doesn't Work: Double-Arrive Deadlock", and the
-//   GEMM page's "Hardware limits": every wave executes exactly the same
-//   sequence of barriers -- the loop below has no wave-dependent branch.
-// * "Xe2 ESIMD GEMM", "Inner-loop rules": no conditionals in the K-loop
-//   (the drain iterations are peeled into their own phase with static wait
-//   counts) and incremented offsets (the buffer descriptors are built once
-//   and only the scalar k offset advances, cf. "Payload CSE").
+//   (2) one s_barrier (the arrival half).
+// * The window between publish and consume ("What goes between arrive and
+//   wait"): right after the publish of tile j+1 each wave starts reading
+//   tile j+1's first operand fragments, runs the last k-step of tile j from
+//   registers (it touches no LDS), and in between issues the copies of tile
+//   j+STAGES into the stage tile j has just vacated.  Nothing in the window
+//   reads LDS another wave is writing or writes LDS another wave reads.
+// * "What Doesn't Work: Double-Arrive Deadlock" and the GEMM page's
+//   "Hardware limits": every wave executes exactly the same sequence of
+//   barriers -- the loop has no wave-dependent branch.
+// * "Xe2 ESIMD GEMM", "Inner-loop rules": no conditionals in the K-loop (the
+//   drain tiles are peeled into their own phase with static wait counts) and
+//   incremented offsets (buffer descriptors are built once and only the
+//   scalar k offset advances, cf. "Payload CSE").
 // * "Xe2 ESIMD GEMM", "DPAS / VNNI": the pages pack B for the matrix engine.
 //   Here B stays row-major [k][n] in LDS and ds_read_b64_tr_b16 delivers it
-//   transposed into the MFMA B-operand layout.
+//   transposed into the MFMA operand layout.
 //
 // Tiling: BM x BN workgroup tile, 4 waves in a WM x WN grid, each wave owns
 // (BM/WM) x (BN/WN) built from 32x32 MFMA blocks (v_mfma_f32_32x32x16).
@@ -48,6 +52,7 @@ struct GemmArgs {
     long long strideA, strideB, strideC;   // elements between batch entries
     int tiles_m, tiles_n;
     int group_m;                           // tile rows per group in the walk order
+    int c_vec;                             // C rows 16-byte aligned: vector stores allowed
 };
 
 // ---------------------------------------------------------------------------
@@ -78,13 +83,19 @@ __device__ inline void tile_of(int pid, int num, int tiles_m, int tiles_n, int g
 // fixes where a lane's 16 bytes land (base + 16*lane), so the swizzle is
 // applied by choosing which global chunk each lane fetches.
 //
-// A tile rows are BK=64 halves (8 chunks).  ds_read_b128 of 32 consecutive
-// rows at one k-chunk must spread over the banks: chunk ^ f(row) with
-// f(row) = (row & 7) ^ ((row >> 3) & 1) gives distinct banks for any 8
-// consecutive rows (32-bank view) and any 16 consecutive rows (64-bank view).
-__device__ inline int swz_a64(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// A rows are BK halves.  ds_read_b128 of 32 consecutive rows at one k-chunk
+// must spread over the banks whether the hardware serves 8 lanes (128 B) or
+// 16 lanes (256 B) of a 16-byte read per cycle:
+//   BK = 64 (8 chunks, 128 B rows): chunk ^ ((row & 7) ^ ((row >> 3) & 1))
+//   BK = 32 (4 chunks,  64 B rows): chunk ^ (((row >> 1) ^ (row >> 3)) & 3)
+template <int BK>
+__device__ inline int swz_a(int row);
+template <>
+__device__ inline int swz_a<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <>
+__device__ inline int swz_a<32>(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// B tile rows are BN halves (>= 16 chunks).  ds_read_b64_tr_b16 makes each
+// B rows are BN halves (>= 16 chunks).  ds_read_b64_tr_b16 makes each
 // 16-lane group read 4 consecutive k rows x 32 bytes; f(k & 3) from
 // {0, 6, 10, 12} puts those 4 rows on disjoint banks in both views, and the
 // two 16-lane groups of a half-wave (next 16 columns) as well.
@@ -95,8 +106,8 @@ __device__ inline int swz_b(int k) {
 template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT>
 struct PipelinedGemm {
     static_assert(WM * WN == 4, "four waves per workgroup");
-    static_assert(BK == 64, "A swizzle is written for 64-wide K tiles");
-    static constexpr int kThreads = 256;
+    static_assert(BK == 64 || BK == 32, "A swizzles exist for 32- and 64-wide K tiles");
+    static_assert(STAGES >= 2, "the window needs at least two stages");
     static constexpr int TM = BM / WM;          // wave tile rows
     static constexpr int TN = BN / WN;          // wave tile cols
     static constexpr int MB = TM / 32;          // 32x32 blocks per wave (m)
@@ -104,24 +115,44 @@ struct PipelinedGemm {
     static constexpr int KS = BK / 16;          // MFMA k-steps per tile
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(BN >= 128, "B swizzle needs >= 16 chunks per row");
+    static_assert(KS % 2 == 0, "fragment double-buffering alternates sets per k-step");
 
     static constexpr int A_STAGE = BM * BK;     // halves
     static constexpr int B_STAGE = BK * BN;
-    static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int LDS_HALVES = STAGES * STAGE;
+    static constexpr int STAGE_BYTES = (A_STAGE + B_STAGE) * 2;
+    static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 
     // LDS-DMA bookkeeping: one wave instruction moves 1 KiB = 512 halves.
-    static constexpr int A_INST = A_STAGE / 512;           // per workgroup
-    static constexpr int B_INST = B_STAGE / 512;
-    static constexpr int A_INST_W = A_INST / 4;            // per wave
-    static constexpr int B_INST_W = B_INST / 4;
-    static constexpr int LOADS_PER_STAGE = A_INST_W + B_INST_W;  // vmcnt units per stage
-    static constexpr int A_ROWS_PER_INST = 512 / BK;       // 8
-    static constexpr int B_ROWS_PER_INST = 512 / BN;       // 2 for BN=256
+    static constexpr int A_INST_W = A_STAGE / 512 / 4;     // per wave
+    static constexpr int B_INST_W = B_STAGE / 512 / 4;
+    static constexpr int LPS = A_INST_W + B_INST_W;         // vmcnt units per stage per wave
+    static constexpr int A_CHUNKS = BK / 8;                 // 16-byte chunks per A row
+    static constexpr int A_ROWS_PER_INST = 64 / A_CHUNKS;
     static constexpr int B_CHUNKS = BN / 8;
-    static_assert(A_INST % 4 == 0 && B_INST % 4 == 0, "stage must split evenly over 4 waves");
-    static_assert(LOADS_PER_STAGE * (STAGES - 1) < 64, "vmcnt is 6 bits");
-    static_assert(KS % 2 == 0, "fragment double-buffering alternates sets per k-step");
+    static constexpr int B_ROWS_PER_INST = 64 / B_CHUNKS;
+    static_assert(A_STAGE % 2048 == 0 && B_STAGE % 2048 == 0, "stage must split evenly over 4 waves");
+    static_assert(LPS * STAGES < 64, "vmcnt is 6 bits");
+
+    // per k-step: MFMAs, LDS reads (A fragments + two B half-fragments each)
+    static constexpr int NMMA = MB * NB;
+    static constexpr int NREAD = MB + 2 * NB;
+    static constexpr int RPM = (NREAD + (NMMA / 2) - 1) / (NMMA / 2);   // reads per MFMA
+    // copies of one group are spread over the KS k-steps of a tile: DSLICE per
+    // k-step, one every DEVERY MFMA slots, starting DOFF slots in
+    static constexpr int DSLICE = LPS / KS;
+    static constexpr int DPQ = (DSLICE + NMMA - 1) / NMMA;              // copies per MFMA slot
+    static constexpr int DEVERY = (NMMA * DPQ) / DSLICE;
+    static constexpr int DOFF = DEVERY / 2;
+    static_assert(LPS % KS == 0, "copies split evenly over the k-steps");
+
+    // epilogue staging: each wave writes its tile to LDS, then stores rows
+    // with 16-byte accesses; 4-byte outputs go in two passes.
+    static constexpr int EPI_PASSES = sizeof(OutT) == 4 ? 2 : 1;
+    static constexpr int EPI_ROWS = TM / EPI_PASSES;
+    static constexpr int EPI_PITCH = TN * (int)sizeof(OutT) + 16;   // bytes, padded
+    static constexpr int EPI_BYTES = 4 * EPI_ROWS * EPI_PITCH;
+    static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 
     typedef typename Mfma<T>::frag_t frag_t;
 };
@@ -130,7 +161,9 @@ template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typena
 __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     typedef PipelinedGemm<T, BM, BN, BK, STAGES, WM, WN, OutT> G;
     typedef typename G::frag_t frag_t;
-    __shared__ __attribute__((aligned(1024))) T lds[G::LDS_HALVES];
+    constexpr int MB = G::MB, NB = G::NB, LPS = G::LPS;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
+    BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -138,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    // ---- a2: tile mapping --------------------------------------------------
+    // ---- a2: tile mapping ----------------------------------------------------
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
     const int m0 = tm * BM;
@@ -158,8 +191,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     uint32_t voffA[G::A_INST_W];
 #pragma unroll
     for (int i = 0; i < G::A_INST_W; ++i) {
-        int row = (wave * G::A_INST_W + i) * G::A_ROWS_PER_INST + lane / 8;
-        int chunk = (lane % 8) ^ swz_a64(row);
+        int row = (wave * G::A_INST_W + i) * G::A_ROWS_PER_INST + lane / G::A_CHUNKS;
+        int chunk = (lane % G::A_CHUNKS) ^ swz_a<BK>(row);
         voffA[i] = (uint32_t)(((m0 + row) * lda + chunk * 8) * 2);
     }
     uint32_t voffB[G::B_INST_W];
@@ -173,20 +206,20 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     const uint32_t b_step = (uint32_t)BK * ldb * 2;
 
     // LDS read offsets (bytes, within a stage) for the MFMA operands.
-    // A block mb, k-step ks: row = wm*TM + mb*32 + lane%32, k = ks*16 + 8*(lane/32).
+    // A block mb, k-step ks: row wm*TM + mb*32 + lane%32, k ks*16 + 8*(lane/32).
     uint32_t rdA[G::KS];
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
         int row = wm * G::TM + (lane % 32);
-        int chunk = (ks * 2 + lane / 32) ^ swz_a64(row);
+        int chunk = (ks * 2 + lane / 32) ^ swz_a<BK>(row);
         rdA[ks] = (uint32_t)((row * BK + chunk * 8) * 2);
     }
     // B block nb: a 16-lane group g reads rows k = ks*16 + 8*(g/2) + 4*h + j/4
     // and columns n = nb*32 + 16*(g%2) + 4*(j%4) (j = lane % 16); the
     // transpose read hands lane j the 4 k-values of column nb*32+16*(g%2)+j.
-    uint32_t rdB[G::NB];
+    uint32_t rdB[NB];
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
         int g = lane / 16, j = lane % 16;
         int krow = 8 * (g / 2) + j / 4;
         int col = wn * G::TN + nb * 32 + 16 * (g % 2) + 4 * (j % 4);
@@ -194,17 +227,12 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         rdB[nb] = (uint32_t)(G::A_STAGE * 2 + krow * BN * 2 + chunk * 16 + (col % 8) * 2);
     }
 
-    BPT_LDS char* lds_bytes = (BPT_LDS char*)lds;
-
-    // LDS byte address of the ring (uniform)
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_bytes));
-    constexpr int STAGE_BYTES = G::STAGE * 2;
-    constexpr int LPS = G::LOADS_PER_STAGE;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
     // copy number i (0 .. LPS-1) of this wave for the tile at k offsets
     // (kA, kB) into ring stage `stage`: A instructions first, then B
-    auto dma_one = [&](int stage, int i, uint32_t kA, uint32_t kB) {
-        const uint32_t sbase = lds0 + stage * STAGE_BYTES;
+    auto dma_one = [&](int stage, int i, uint32_t kA, uint32_t kB) __attribute__((always_inline)) {
+        const uint32_t sbase = lds0 + stage * G::STAGE_BYTES;
         if (i < G::A_INST_W)
             dma16(rsA, sbase + (wave * G::A_INST_W + i) * 1024, voffA[i], kA);
         else
@@ -212,47 +240,59 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
                   voffB[i - G::A_INST_W], kB);
     };
 
-    float16_t acc[G::MB][G::NB];
+    float16_t acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < G::MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < G::NB; ++j)
+        for (int j = 0; j < NB; ++j)
             acc[i][j] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                                   0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-    // Operand fragments of one MFMA k-step, double-buffered in registers.
-    frag_t fa0[G::MB], fb0[G::NB], fa1[G::MB], fb1[G::NB];
+    // Operand fragments of one k-step, double-buffered: set 0 and set 1.
+    frag_t fa[2][MB];
+    short4_t fbl[2][NB], fbh[2][NB];
 
-    auto load_frags = [&](int stage, int ks, frag_t (&a)[G::MB], frag_t (&b)[G::NB]) {
-        BPT_LDS char* sbase = lds_bytes + stage * STAGE_BYTES;
-#pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb)
-            a[mb] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + mb * 32 * BK * 2);
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) {
-            BPT_LDS char* p = sbase + rdB[nb] + ks * 16 * BN * 2;
-            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
-            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
-            b[nb] = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    // LDS read number p (0 .. NREAD-1) of k-step ks of ring stage st into set s
+    auto read_piece = [&](int st, int ks, int p, int s) __attribute__((always_inline)) {
+        BPT_LDS char* sbase = lds + st * G::STAGE_BYTES;
+        if (p < MB) {
+            fa[s][p] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + p * 32 * BK * 2);
+        } else {
+            const int nb = (p - MB) / 2, h = (p - MB) % 2;
+            BPT_LDS short4_t* q = (BPT_LDS short4_t*)(sbase + rdB[nb] + ks * 16 * BN * 2 + h * 4 * BN * 2);
+            if (h == 0) fbl[s][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q);
+            else fbh[s][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q);
         }
     };
 
-    // All MFMAs of one k-step; when `with_dma`, the next-next tile's copies
-    // are issued between them (ceil(LPS / MFMAs) per MFMA).
-    constexpr int NMMA = G::MB * G::NB;
-    constexpr int DMA_PER_MMA = (LPS + NMMA - 1) / NMMA;
-    auto mma_step = [&](frag_t (&a)[G::MB], frag_t (&b)[G::NB], bool with_dma, int stage,
-                        uint32_t kA, uint32_t kB) {
+    // One k-step: the MFMAs on fragment set s, interleaved with RPM LDS reads
+    // per MFMA for (rst, rks) into the other set (when `reads`) and with
+    // copies number [d0, d0 + DSLICE) of the group for stage dst (when
+    // `dma`), one every NMMA/DSLICE MFMAs.  The MFMA takes the B fragment as
+    // its first operand, so that each lane's result holds four consecutive
+    // columns of one row of C.
+    auto kstep = [&](int s, bool reads, int rst, int rks, bool dma, int dst, int d0, uint32_t kA,
+                     uint32_t kB) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < NMMA; ++q) {
-            const int mb = q / G::NB, nb = q % G::NB;
-            acc[mb][nb] = Mfma<T>::mma32(a[mb], b[nb], acc[mb][nb]);
-            if (with_dma) {
+        for (int q = 0; q < G::NMMA; ++q) {
+            if (reads) {
 #pragma unroll
-                for (int r = 0; r < DMA_PER_MMA; ++r)
-                    if (q * DMA_PER_MMA + r < LPS) dma_one(stage, q * DMA_PER_MMA + r, kA, kB);
-                __builtin_amdgcn_sched_barrier(0);     // keep copies spread between MFMAs
+                for (int r = 0; r < G::RPM; ++r)
+                    if (q * G::RPM + r < G::NREAD) read_piece(rst, rks, q * G::RPM + r, s ^ 1);
             }
+            const int mb = q / NB, nb = q % NB;
+            frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb],
+                                                                          0, 1, 2, 3, 4, 5, 6, 7));
+            acc[mb][nb] = Mfma<T>::mma32(b, fa[s][mb], acc[mb][nb]);
+            if (dma) {
+#pragma unroll
+                for (int r = 0; r < G::DPQ; ++r) {
+                    const int slot = q * G::DPQ + r - G::DOFF;   // copy slot within the slice
+                    if (slot >= 0 && slot % G::DEVERY == 0 && slot / G::DEVERY < G::DSLICE)
+                        dma_one(dst, d0 + slot / G::DEVERY, kA, kB);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep this interleave as written
         }
     };
 
@@ -263,10 +303,13 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     // Then comes the publish point of tile j+1 and its window:
     //   publish(j+1): own copies of tile j+1 landed + s_barrier.  Every wave
     //                 has also finished its reads of tile j's stage.
-    //   window:       read tile j+1's first fragments, then run tile j's last
-    //                 k-step from registers while issuing the copies of tile
+    //   window:       read tile j+1's first fragments, run tile j's last
+    //                 k-step from registers, and start the copies of tile
     //                 j+STAGES into the stage tile j just vacated.
-    // The copies of a tile are in flight for STAGES-1 full tiles of MFMA work.
+    // The copies of tile j+STAGES are spread in KS slices: slice 0 in the
+    // window, slices 1 .. KS-1 in k-steps 0 .. KS-2 of tile j+1, so the load
+    // path never sees a burst.  All of them are issued before publish(j+2),
+    // which therefore still waits for exactly STAGES-2 younger groups.
     const int nk = K / BK;                 // host guarantees K % BK == 0 and nk >= STAGES
     uint32_t kA = 0, kB = 0;               // byte offsets of the next tile to copy
 #pragma unroll
@@ -277,71 +320,108 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         kB += b_step;
     }
     publish<LPS * (STAGES - 1)>();         // tile 0 is in LDS for every wave
-    load_frags(0, 0, fa0, fb0);
-    int sc = 0;                            // stage of the tile being consumed
-
-    // one tile; DMA: issue tile j+STAGES in the window; VM: vmcnt for
-    // publish(j+1); LAST: final tile (no publish, no next reads)
-    auto tile = [&]<bool DMA, int VM, bool LAST>() {
 #pragma unroll
-        for (int ks = 0; ks < G::KS - 1; ++ks) {
-            // the next k-step's reads are issued before this k-step's MFMAs
-            // (the fence stops the scheduler from sinking them to their use)
-            if (ks % 2 == 0) {
-                load_frags(sc, ks + 1, fa1, fb1);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_step(fa0, fb0, false, 0, 0, 0);
-            } else {
-                load_frags(sc, ks + 1, fa0, fb0);
-                __builtin_amdgcn_sched_barrier(0);
-                mma_step(fa1, fb1, false, 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int p = 0; p < G::NREAD; ++p) read_piece(0, 0, p, 0);
+    int sc = 0;                            // stage of the tile being consumed
+    int sp = 0;                            // stage of the group still being copied
+    uint32_t kAp = 0, kBp = 0;             // and its k offsets
+
+    // one tile.  WIN: start a new group (tile j+STAGES) in the window; PEND:
+    // finish the group started in the previous window during k-steps
+    // 0 .. KS-2; VM: vmcnt for publish(j+1); LAST: final tile (no publish, no
+    // next reads).
+    auto tile = [&]<bool WIN, bool PEND, int VM, bool LAST>() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < G::KS - 1; ++ks)
+            kstep(ks & 1, true, sc, ks + 1, PEND, sp, (ks + 1) * G::DSLICE, kAp, kBp);
         if constexpr (!LAST) {
             publish<VM>();
             const int sn = (sc + 1 == STAGES) ? 0 : sc + 1;
-            load_frags(sn, 0, fa0, fb0);
-            __builtin_amdgcn_sched_barrier(0);
-            mma_step(fa1, fb1, DMA, sc, kA, kB);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (DMA) {
+            kstep(1, true, sn, 0, WIN, sc, 0, kA, kB);
+            if constexpr (WIN) {
+                sp = sc;
+                kAp = kA;
+                kBp = kB;
                 kA += a_step;
                 kB += b_step;
             }
             sc = sn;
         } else {
-            mma_step(fa1, fb1, false, 0, 0, 0);
+            kstep(1, false, 0, 0, false, 0, 0, 0, 0);
         }
     };
 
-    for (int j = 0; j < nk - STAGES; ++j) tile.template operator()<true, LPS * (STAGES - 2), false>();
-    // drain: the last STAGES tiles issue no copies; the wait counts fall to 0
+    constexpr int VMS = LPS * (STAGES - 2);
+    if (nk > STAGES) {
+        tile.template operator()<true, false, VMS, false>();
+        for (int j = 1; j < nk - STAGES; ++j) tile.template operator()<true, true, VMS, false>();
+        tile.template operator()<false, true, VMS, false>();      // drain tile 0 finishes the last group
+    } else {
+        tile.template operator()<false, false, VMS, false>();
+    }
+    // the rest of the drain, tiles d = 1 .. STAGES-1 of it: no copies; the
+    // wait count of publish falls by one group per tile, and the last tile
+    // publishes nothing
+    constexpr auto drain_vm = [](int d) constexpr { return d < STAGES - 1 ? LPS * (STAGES - 2 - d) : 0; };
     [&]<int... D>(std::integer_sequence<int, D...>) {
-        ((D < STAGES - 1 ? tile.template operator()<false, LPS * (STAGES - 2 - (D < STAGES - 1 ? D : 0)), false>()
-                         : tile.template operator()<false, 0, true>()),
+        ((D + 1 < STAGES - 1 ? tile.template operator()<false, false, drain_vm(D + 1), false>()
+                             : tile.template operator()<false, false, 0, true>()),
          ...);
-    }(std::make_integer_sequence<int, STAGES>{});
+    }(std::make_integer_sequence<int, STAGES - 1>{});
 
     // ---- a8: epilogue ---------------------------------------------------------
-    // 32x32 block result layout: lane l, register r holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // Result layout (B fragment as first MFMA operand): lane l, register r of
+    // block (mb, nb) holds row mb*32 + l%32, column nb*32 + 8*(r/4) +
+    // 4*(l/32) + r%4 of the wave tile.  Each wave stages its tile in LDS
+    // (row-major, padded rows) and then writes whole rows, 16 bytes a lane.
+    publish<0>();                          // every wave is done with the ring
     OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
     const int ldc = args.ldc;
-    const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+    const int row0 = m0 + wm * G::TM;      // first C row / column of this wave
+    const int col0 = n0 + wn * G::TN;
+    const bool vec = args.c_vec && (row0 + G::TM <= M) && (col0 + G::TN <= N);
+    BPT_LDS char* stage_w = lds + wave * (G::EPI_ROWS * G::EPI_PITCH);
+    constexpr int OB = (int)sizeof(OutT);
+    constexpr int CH_PER_ROW = G::TN * OB / 16;            // 16-byte chunks per wave-tile row
+    constexpr int ROWS_PER_IT = 64 / CH_PER_ROW;
+    typedef OutT out4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
+    for (int pass = 0; pass < G::EPI_PASSES; ++pass) {
+        constexpr int MBP = MB / G::EPI_PASSES;
 #pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) {
-            int col = n0 + wn * G::TN + nb * 32 + (lane % 32);
-            int rbase = m0 + wm * G::TM + mb * 32 + 4 * (lane / 32);
+        for (int mbp = 0; mbp < MBP; ++mbp) {
+            const int mb = pass * MBP + mbp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int row = rbase + 8 * (r / 4) + (r % 4);
-                if (full || (row < M && col < N))
-                    Cb[(long long)row * ldc + col] = cvt_out<OutT>(acc[mb][nb][r]);
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    out4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = cvt_out<OutT>(acc[mb][nb][4 * g + e]);
+                    const int r = mbp * 32 + (lane % 32);
+                    const int c = nb * 32 + 8 * g + 4 * (lane / 32);
+                    *(BPT_LDS out4_t*)(stage_w + r * G::EPI_PITCH + c * OB) = v;
+                }
+        }
+#pragma unroll
+        for (int it = 0; it < G::EPI_ROWS / ROWS_PER_IT; ++it) {
+            const int r = it * ROWS_PER_IT + lane / CH_PER_ROW;
+            const int ch = lane % CH_PER_ROW;
+            int4_t v = *(BPT_LDS int4_t*)(stage_w + r * G::EPI_PITCH + ch * 16);
+            const int grow = row0 + pass * G::EPI_ROWS + r;
+            const int gcol = col0 + ch * (16 / OB);
+            OutT* dst = Cb + (long long)grow * ldc + gcol;
+            if (vec) {
+                *(int4_t*)dst = v;
+            } else if (grow < M) {
+                OutT vals[16 / OB];
+                __builtin_memcpy(vals, &v, 16);
+#pragma unroll
+                for (int e = 0; e < 16 / OB; ++e)
+                    if (gcol + e < N) dst[e] = vals[e];
             }
         }
+    }
 }
 
 }  // namespace bpt

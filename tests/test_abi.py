@@ -118,15 +118,21 @@ def test_forced_variant_that_cannot_take_the_call(L):
 
 def test_automatic_variant_choice():
     v = pkg.variants()
-    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == v["pipelined_256x256x64_s2"]
-    assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == v["pipelined_256x256x64_s2"]
-    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == v["pipelined_256x256x64_s2"]
-    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256) == v["pipelined_128x128x64_s2"]
+    big = v["pipelined_256x256x32_s4"]
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == big
+    assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == big
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == big
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256) == v["pipelined_128x128x32_s4"]
+    # K = 96: three 32-wide tiles (< 4 stages) and not a multiple of 64
+    assert pkg.select_variant("f16", 1, 256, 256, 96, 96, 256) == v["generic_64x64x16"]
+    # K = 128: four 32-wide tiles fill the four-stage ring
+    assert pkg.select_variant("f16", 1, 4096, 4096, 128, 128, 4096) == big
     # K not a multiple of 64, odd leading dimension, unaligned base: generic
     assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == v["generic_64x64x16"]
-    # K = 64 is one K-tile, fewer than the two ring stages
+    # K = 64 is one 64-wide tile (two stages need two) and two 32-wide tiles
+    # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
     # rejected / nothing to do
     assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0

@@ -64,12 +64,14 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
         assert np.array_equal(as_bits(got), oracle.encode(ref, dtype))
 
 
-VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2"]
-# the pipelined variants need K % 64 == 0, K >= 128 (two ring stages) and
+VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
+            "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4"]
+# the pipelined variants need K to be a multiple of the K-tile spanning at
+# least as many tiles as ring stages (K >= 160 covers every variant) and
 # 16-byte aligned rows (ld % 8 == 0); M is free, and a ragged N is exercised
 # with a padded ldb below
-SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 128), (1, 8, 128), (33, 520, 192),
-               (129, 136, 128), (640, 768, 512), (256, 512, 1024)]
+SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 192), (1, 8, 256), (33, 520, 192),
+               (129, 136, 256), (640, 768, 512), (256, 512, 1024)]
 SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64)]
 
 
@@ -158,7 +160,7 @@ def test_k_zero_writes_zeros_and_empty_is_noop():
 @pytest.mark.parametrize("vname", VARIANTS)
 def test_batched_small(vname):
     v = pkg.variants()[vname]
-    b, M, N, K = 3, 160, 192, 128
+    b, M, N, K = 3, 160, 192, 192
     say(f"[batched] {vname}")
     A = inputs.uniform((b, M, K), 7001, lo=-0.5, hi=0.5)
     B = inputs.uniform((b, K, N), 7002, lo=-0.5, hi=0.5)
