@@ -41,6 +41,21 @@ def build(out: str = LIB_PATH, extra: list[str] | None = None) -> str:
     return out
 
 
+CALIB_SRC = os.path.join(CSRC, "calib.hip")
+CALIB_PATH = os.path.join(PKG_DIR, "calib")
+
+
+def build_calib(out: str = CALIB_PATH) -> str:
+    """Compile the measurement companion (copy-kernel counter calibration and
+    the MFMA throughput/clock probe); not part of the library."""
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out, CALIB_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr[-6000:]}")
+    return out
+
+
 def device_asm(out_dir: str) -> str:
     """Emit the gfx950 assembly of the library into out_dir; returns the .s path."""
     os.makedirs(out_dir, exist_ok=True)
@@ -56,3 +71,4 @@ def device_asm(out_dir: str) -> str:
 
 if __name__ == "__main__":
     print(build())
+    print(build_calib())

@@ -38,6 +38,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_sha() -> str:
+    """Hash of the sources the pipelined kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("gemm_pipelined.hpp", "device_common.hpp", "api.hip"):
+        with open(os.path.join(ROOT, "barrier_pipelined_tiled_amd", "csrc", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
+    scaled by the copy-kernel calibration; None when no run exists for this
+    kernel or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get("entries", {}).get(workload)
+    if not e or e.get("kernel") != kernel or e.get("source_sha") != kernel_source_sha():
+        return None
+    return int(round((e["fetch_kib"] * t["fetch_scale"] + e["write_kib"] * t["write_scale"]) * 1024))
+
+
 def cpu_baseline(w, A, B, budget_s: float = 12.0):
     """Time the oracle on the first R rows of A times all of B (set 0)."""
     import oracle
@@ -148,6 +173,7 @@ def main():
 
     variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.N, w.out_fp32)
     names = {v: k for k, v in pkg.variants().items()}
+    roof["traffic"] = measured_traffic(w.name, names.get(variant_id, ""))
 
     cpu = None
     if not args.no_cpu_baseline:
