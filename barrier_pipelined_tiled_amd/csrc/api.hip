@@ -12,6 +12,7 @@
 #include "../../include/bpt_gemm.h"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
+#include "gemm_skinny.hpp"
 
 namespace {
 
@@ -36,7 +37,8 @@ enum Variant {
     V_PIPE_256_K32_S4 = 4,  // 256x256 tile, BK 32, 4 stages
     V_PIPE_256_K32_S5 = 5,  // 256x256 tile, BK 32, 5 stages
     V_PIPE_128_K32_S4 = 6,  // 128x128 tile, BK 32, 4 stages
-    V_COUNT = 6
+    V_SKINNY = 7,           // 64x32 tile over all of K, 8 waves split K, per-wave LDS rings
+    V_COUNT = 7
 };
 
 const char* const kVariantNames[] = {
@@ -47,11 +49,13 @@ const char* const kVariantNames[] = {
     "pipelined_256x256x32_s4",
     "pipelined_256x256x32_s5",
     "pipelined_128x128x32_s4",
+    "skinny_64x32_w8_k32_s4",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0};
+
 
 struct Call {
     int dtype;
@@ -68,8 +72,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // Can a pipelined variant with K-tile BK and STAGES ring stages take this
 // call?  The prologue fills every stage, so K must span at least STAGES tiles.
+// Column chunks of B are 8 wide and must not straddle N: N % 8 == 0.
 bool pipelined_ok(const Call& c, int BK, int STAGES) {
     if (c.K <= 0 || c.K % BK != 0 || c.K / BK < STAGES) return false;
+    if (c.N % 8 != 0) return false;
     if (!aligned16(c.A) || !aligned16(c.B)) return false;
     if (c.lda % 8 != 0 || c.ldb % 8 != 0) return false;
     if (c.sA % 8 != 0 || c.sB % 8 != 0) return false;
@@ -81,8 +87,25 @@ bool pipelined_ok(const Call& c, int BK, int STAGES) {
     return true;
 }
 
+// the skinny kernel: 8 waves split K, 32-deep chunks, 4 B stages per wave
+constexpr int kSkWaves = 8, kSkChunk = 32, kSkStages = 4;
+
+bool skinny_ok(const Call& c) {
+    if (c.K <= 0 || c.K % (kSkWaves * kSkChunk) != 0) return false;
+    if (c.K / (kSkWaves * kSkChunk) < kSkStages) return false;
+    if (c.N % 8 != 0) return false;
+    if (!aligned16(c.A) || !aligned16(c.B)) return false;
+    if (c.lda % 8 != 0 || c.ldb % 8 != 0 || c.sA % 8 != 0 || c.sB % 8 != 0) return false;
+    long long extA = ((c.M + 64) * c.lda + c.K) * 2;
+    long long extB = (c.K * c.ldb + c.N + 64) * 2;
+    return extA <= kI31 && extB <= kI31;
+}
+
 int choose(const Call& c) {
     long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
+    // few rows of A: stream B once with the K-split skinny kernel when that
+    // yields at least half a workgroup per CU
+    if (c.M <= 64 && (c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
     const bool big = tiles256 >= 128;
     if (big && pipelined_ok(c, 32, 4)) return V_PIPE_256_K32_S4;
     if (pipelined_ok(c, 32, 4)) return V_PIPE_128_K32_S4;
@@ -110,6 +133,25 @@ hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
         hipLaunchKernelGGL((bpt::gemm_pipelined_kernel<T, BM, BN, BK, STAGES, 2, 2, OutT>),
                            dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t launch_skinny(const Call& c, hipStream_t stream) {
+    bpt::SkinnyArgs a;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_n = (int)((c.N + 31) / 32);
+    const long long tm = (c.M + 63) / 64;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        a.A = static_cast<const T*>(c.A) + b0 * c.sA;
+        a.B = static_cast<const T*>(c.B) + b0 * c.sB;
+        a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
+        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSkWaves, kSkChunk, kSkStages, OutT>),
+                           dim3((unsigned)a.tiles_n, (unsigned)tm, (unsigned)nb), dim3(kSkWaves * 64), 0, stream, a);
     }
     return hipGetLastError();
 }
@@ -155,6 +197,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PIPE_256_K32_S4: return launch_pipelined<T, OutT, 256, 256, 32, 4>(c, stream);
         case V_PIPE_256_K32_S5: return launch_pipelined<T, OutT, 256, 256, 32, 5>(c, stream);
         case V_PIPE_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4>(c, stream);
+        case V_SKINNY: return launch_skinny<T, OutT>(c, stream);
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -182,6 +225,7 @@ bpt_status validate(const Call& c) {
 bool variant_accepts(const Call& c, int v) {
     switch (v) {
         case V_GENERIC: return true;
+        case V_SKINNY: return skinny_ok(c);
         default:
             if (v > V_GENERIC && v <= V_COUNT) return pipelined_ok(c, kVariantBK[v], kVariantStages[v]);
             return false;

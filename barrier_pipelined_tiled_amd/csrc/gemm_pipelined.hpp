@@ -195,12 +195,17 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         int chunk = (lane % G::A_CHUNKS) ^ swz_a<BK>(row);
         voffA[i] = (uint32_t)(((m0 + row) * lda + chunk * 8) * 2);
     }
+    // A lane whose 8 columns of B start at or past N fetches the last
+    // in-bounds chunk instead (host: N % 8 == 0), so no copy ever reads past
+    // the end of B; those columns of C are never stored.
     uint32_t voffB[G::B_INST_W];
 #pragma unroll
     for (int i = 0; i < G::B_INST_W; ++i) {
         int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
         int chunk = (lane % G::B_CHUNKS) ^ swz_b(row);
-        voffB[i] = (uint32_t)((row * ldb + n0 + chunk * 8) * 2);
+        int col = n0 + chunk * 8;
+        if (col >= N) col = N - 8;
+        voffB[i] = (uint32_t)((row * ldb + col) * 2);
     }
     const uint32_t a_step = BK * 2;                        // bytes per K-tile
     const uint32_t b_step = (uint32_t)BK * ldb * 2;

@@ -1,0 +1,227 @@
+// gemm_skinny.hpp -- the memory-bound GEMM for few rows of A (decode-like
+// shapes, e.g. 64 x 8192 x 8192): C (M x N) = A (M x K) * B (K x N).
+//
+// Such a product is bound by streaming B (K x N) from HBM once; A is small and
+// stays in L2.  To keep all 256 CUs streaming, a workgroup owns a 64 x 32
+// output block over ALL of K (N/32 workgroups), and its 8 waves split K into
+// 8 slices ("split-K inside the workgroup").  Each wave streams its slice
+// through private LDS rings -- a 4-stage ring for B chunks and a 2-slot ring
+// for A chunks -- filled by LDS-DMA, so the loop needs no workgroup barrier:
+// a stage is published to the only wave that reads it by that wave's own
+// vmcnt wait (the "bytes pending" half of the mbarrier page's completion
+// rule; nobody else has to arrive).  Everything asynchronous lands in LDS,
+// never in registers, so no copy of an in-flight register can be made.  At
+// the end the 8 partial 64 x 32 tiles are summed through LDS in a fixed wave
+// order (deterministic, no atomics, no workspace), converted and stored.
+#pragma once
+#include "device_common.hpp"
+#include "gemm_pipelined.hpp"   // swz_a
+
+namespace bpt {
+
+struct SkinnyArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    long long strideA, strideB, strideC;
+    int tiles_n;
+};
+
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <typename T, int WAVES, int KC, int SB, typename OutT>
+struct SkinnyGemm {
+    static_assert(KC == 32, "A rows of 64 bytes (the 32-wide swizzle)");
+    static_assert(SB >= 3, "B runs at least two chunks ahead of A");
+    static constexpr int BM = 64, BN = 32;          // two 32x32 MFMA blocks
+    static constexpr int KSTEPS = KC / 16;          // MFMA k-steps per chunk
+    static constexpr int A_BYTES = BM * KC * 2;     // 4 KiB per A chunk
+    static constexpr int B_BYTES = KC * BN * 2;     // 2 KiB per B chunk
+    static constexpr int LA = A_BYTES / 1024;       // copies per A chunk
+    static constexpr int LB = B_BYTES / 1024;       // copies per B chunk
+    static constexpr int WAVE_LDS = 2 * A_BYTES + SB * B_BYTES;
+    static constexpr int RING_BYTES = WAVES * WAVE_LDS;
+    static constexpr int RED_BYTES = WAVES * BM * BN * 4;
+    static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    typedef typename Mfma<T>::frag_t frag_t;
+};
+
+template <typename T, int WAVES, int KC, int SB, typename OutT>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs args) {
+    typedef SkinnyGemm<T, WAVES, KC, SB, OutT> G;
+    typedef typename G::frag_t frag_t;
+    constexpr int BN = G::BN;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
+    BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // XCD-aware order: consecutive column tiles on the same XCD share L2
+    // lines of B (a 32-column tile reads 64 bytes of each 128-byte line).
+    int pid = blockIdx.x;
+    const int num = gridDim.x;
+    if ((num & 7) == 0) pid = (pid & 7) * (num >> 3) + (pid >> 3);
+    const int n0 = pid * BN;
+    const int m0 = blockIdx.y * G::BM;
+    const int batch = blockIdx.z;
+
+    const T* Ab = static_cast<const T*>(args.A) + batch * args.strideA;
+    const T* Bb = static_cast<const T*>(args.B) + batch * args.strideB;
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
+    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + N) * 2));
+
+    const int kw = K / WAVES;                       // this wave's K slice
+    const int kbase = wave * kw;
+    const int nchunks = kw / KC;                    // host: kw % KC == 0, nchunks >= SB
+
+    // A copies: chunk rows m (64 bytes each), 16 rows per KiB; lane p brings
+    // row 16i + p/4 and lands at 16-byte slot p%4 of it; the global chunk it
+    // fetches is swizzled.  Rows >= M start past num_records and read zeros.
+    uint32_t voffA[G::LA];
+#pragma unroll
+    for (int i = 0; i < G::LA; ++i) {
+        const int row = 16 * i + lane / 4;
+        const int chunk = (lane % 4) ^ swz_a<32>(row);
+        voffA[i] = (uint32_t)(((m0 + row) * lda + kbase + chunk * 8) * 2);
+    }
+    // B copies: chunk rows k (64 bytes = the 32 columns), 16 rows per KiB.
+    // A lane whose 8 columns start at or past N fetches the last in-bounds
+    // chunk instead (host: N % 8 == 0); those columns are never stored.
+    uint32_t voffB[G::LB];
+#pragma unroll
+    for (int i = 0; i < G::LB; ++i) {
+        int col = n0 + 8 * (lane % 4);
+        if (col >= N) col = N - 8;
+        voffB[i] = (uint32_t)(((kbase + 16 * i + lane / 4) * ldb + col) * 2);
+    }
+    const uint32_t astep = KC * 2;                  // bytes per chunk along K
+    const uint32_t bstep = (uint32_t)KC * ldb * 2;
+
+    // this wave's LDS: A slots [0, 2*A_BYTES), then B stages
+    const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * G::WAVE_LDS;
+    BPT_LDS char* wlds_p = lds + wave * G::WAVE_LDS;
+
+    auto issue_a = [&](int c) __attribute__((always_inline)) {
+        const uint32_t dst = wlds + (c & 1) * G::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < G::LA; ++i) dma16(rsA, dst + i * 1024, voffA[i], c * astep);
+    };
+    auto issue_b = [&](int c) __attribute__((always_inline)) {
+        const uint32_t dst = wlds + 2 * G::A_BYTES + (c % SB) * G::B_BYTES;
+#pragma unroll
+        for (int i = 0; i < G::LB; ++i) dma16(rsB, dst + i * 1024, voffB[i], c * bstep);
+    };
+
+    // fragment reads.  A (row block mb, k-step kk): row mb*32 + l%32, chunk
+    // kk*2 + l/32, swizzled.  B: a 16-lane group g reads rows kk*16 + 8*(g/2)
+    // + 4h + j/4, columns 16*(g%2) + 4*(j%4) (j = l%16), transposed.
+    uint32_t rdA[G::KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < G::KSTEPS; ++kk) {
+        const int row = lane % 32;                  // + mb*32 keeps the swizzle
+        rdA[kk] = (uint32_t)(row * KC * 2 + (((kk * 2 + lane / 32) ^ swz_a<32>(row)) * 16));
+    }
+    const int g = lane / 16, j = lane % 16;
+    const uint32_t rdB = (uint32_t)((8 * (g / 2) + j / 4) * BN * 2 + (16 * (g % 2) + 4 * (j % 4)) * 2);
+
+    float16_t acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+        acc[mb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c) __attribute__((always_inline)) {
+        BPT_LDS char* ap = wlds_p + (c & 1) * G::A_BYTES;
+        BPT_LDS char* bp = wlds_p + 2 * G::A_BYTES + (c % SB) * G::B_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < G::KSTEPS; ++kk) {
+            BPT_LDS char* p = bp + rdB + kk * 16 * BN * 2;
+            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
+            frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                frag_t a = *(BPT_LDS frag_t*)(ap + rdA[kk] + mb * 32 * KC * 2);
+                acc[mb] = Mfma<T>::mma32(b, a, acc[mb]);
+            }
+        }
+    };
+
+    // Chunk c: B in stage c % SB, A in slot c % 2.  Issue order per chunk is
+    // A(c+1) then B(c+SB-1), so at the top of chunk c, after A(c) (issued one
+    // chunk earlier) only B(c+SB-2) was issued: vmcnt(LB) covers A(c) and
+    // the older B(c).  The stage and slot refilled in chunk c are those of
+    // chunk c-1, whose reads the lgkmcnt(0) wait has retired.
+    //
+    // prologue = the pattern of chunks -(SB-1) .. -1: B(0 .. SB-3), A(0), B(SB-2)
+#pragma unroll
+    for (int i = 0; i < SB - 2; ++i) issue_b(i);
+    issue_a(0);
+    issue_b(SB - 2);
+
+    int c = 0;
+    for (; c + SB - 1 < nchunks; ++c) {             // steady: both copies exist
+        wait_vm<G::LB>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue_a(c + 1);
+        issue_b(c + SB - 1);
+        compute(c);
+    }
+    // drain, the last SB-1 chunks: no B left to issue.  The first of them
+    // still had B(nchunks-1) issued after its A; after that, A(c) is the
+    // newest copy, so the wait is for everything.
+    wait_vm<G::LB>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue_a(c + 1);
+    compute(c);
+    ++c;
+#pragma unroll
+    for (int d = 1; d < SB - 1; ++d) {
+        wait_vm<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (d + 1 < SB - 1) issue_a(c + 1);         // static: d is unrolled
+        compute(c);
+        ++c;
+    }
+
+    // ---- reduction of the WAVES partial tiles, fixed order ------------------
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // partial of this wave, row-major [64][32] fp32 (lane's 4 consecutive
+    // columns per register group: the B-first MFMA layout)
+    BPT_LDS char* red = lds + wave * (G::BM * BN * 4);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            float4_t v = {acc[mb][4 * gq], acc[mb][4 * gq + 1], acc[mb][4 * gq + 2], acc[mb][4 * gq + 3]};
+            const int r = mb * 32 + lane % 32, col = 8 * gq + 4 * (lane / 32);
+            *(BPT_LDS float4_t*)(red + (r * BN + col) * 4) = v;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
+    constexpr int OUTS = G::BM * BN;                // 2048 outputs, 4 per thread
+    for (int e = tid * 4; e < OUTS; e += WAVES * 64 * 4) {
+        const int r = e / BN, col = e % BN;
+        float4_t s = *(BPT_LDS float4_t*)(lds + (r * BN + col) * 4);
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) s += *(BPT_LDS float4_t*)(lds + w * (G::BM * BN * 4) + (r * BN + col) * 4);
+        const int grow = m0 + r, gcol = n0 + col;
+        if (grow < M) {
+            OutT* dst = Cb + (long long)grow * args.ldc + gcol;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (gcol + q < N) dst[q] = cvt_out<OutT>(s[q]);
+        }
+    }
+}
+
+}  // namespace bpt

@@ -65,17 +65,28 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
-            "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4"]
+            "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
+            "skinny_64x32_w8_k32_s4"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
-# least as many tiles as ring stages (K >= 160 covers every variant) and
-# 16-byte aligned rows (ld % 8 == 0); M is free, and a ragged N is exercised
-# with a padded ldb below
+# least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
+# aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
+# a tile (200, 520, 136 below)
 SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 192), (1, 8, 256), (33, 520, 192),
                (129, 136, 256), (640, 768, 512), (256, 512, 1024)]
-SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64)]
+SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64), (96, 201, 256)]
+
+
+# the skinny variant splits K over 8 waves in 32-deep chunks, 4 per wave at
+# least: K a multiple of 256 and >= 1024; any M (64-row tiles); N % 8 == 0 with
+# a ragged last 32-column tile; chunk counts per wave both below, at and above
+# the ring depth so stages are reused
+SHAPES_SKINNY = [(64, 1024, 2048), (37, 320, 2560), (100, 256, 2048), (1, 512, 4096), (64, 2048, 3072),
+                 (64, 200, 1024), (70, 264, 1280), (64, 256, 8192)]
 
 
 def _shapes(vname):
+    if vname.startswith("skinny"):
+        return SHAPES_SKINNY
     return SHAPES_PIPE + (SHAPES_GENERIC_ONLY if vname.startswith("generic") else [])
 
 
@@ -121,28 +132,32 @@ def test_identity_and_permutation_exact():
     assert torch.equal(run(P, B), B[perm])                 # P B permutes rows
 
 
-def test_padded_leading_dimensions_nan_padding():
+PADDED_CASES = [(v, 70, 200, 2048) if v.startswith("skinny") else (v, 300, 200, 192) for v in VARIANTS] + \
+    [("generic_64x64x16", 300, 201, 200)]
+
+
+@pytest.mark.parametrize("vname,M,N,K", PADDED_CASES)
+def test_padded_leading_dimensions_nan_padding(vname, M, N, K):
     """lda > K, ldb > N, ldc > N with NaN in every padding element: the
     result must be finite and correct, and C's padding must be untouched.
-    N = 201 is not a multiple of 8: the last column chunk of B straddles N."""
-    M, N, K = 300, 201, 192
-    for vname in VARIANTS:
-        v = pkg.variants()[vname]
-        say(f"[padded] {vname}")
-        A = inputs.uniform((M, K), 6001, nonzero=True)
-        B = inputs.uniform((K, N), 6002, nonzero=True)
-        Ap = torch.full((M, K + 8), float("nan"), dtype=torch.float16)
-        Ap[:, :K] = A
-        Bp = torch.full((K, N + 23), float("nan"), dtype=torch.float16)
-        Bp[:, :N] = B
-        Cp = torch.full((M, N + 8), 7.0, dtype=torch.float16, device=DEV)
-        pkg.gemm_ex(Ap.to(DEV)[:, :K], Bp.to(DEV)[:, :N], Cp[:, :N], variant=v)
-        torch.cuda.synchronize()
-        Cp = Cp.cpu()
-        assert torch.all(Cp[:, N:] == 7.0)
-        ref = oracle.gemm(inputs.bits(A), inputs.bits(B))
-        m = oracle.compare(Cp[:, :N].float().numpy(), ref, K)
-        assert m["ok"], (vname, m)
+    N = 200 ends inside the last column tile of every fast variant; the
+    guarded kernel also takes N = 201 and K = 200."""
+    v = pkg.variants()[vname]
+    say(f"[padded] {vname} M={M} N={N} K={K}")
+    A = inputs.uniform((M, K), 6001, nonzero=True)
+    B = inputs.uniform((K, N), 6002, nonzero=True)
+    Ap = torch.full((M, K + 8), float("nan"), dtype=torch.float16)
+    Ap[:, :K] = A
+    Bp = torch.full((K, N + 24), float("nan"), dtype=torch.float16)
+    Bp[:, :N] = B
+    Cp = torch.full((M, N + 8), 7.0, dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(Ap.to(DEV)[:, :K], Bp.to(DEV)[:, :N], Cp[:, :N], variant=v)
+    torch.cuda.synchronize()
+    Cp = Cp.cpu()
+    assert torch.all(Cp[:, N:] == 7.0)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B))
+    m = oracle.compare(Cp[:, :N].float().numpy(), ref, K)
+    assert m["ok"], (vname, m)
 
 
 def test_k_zero_writes_zeros_and_empty_is_noop():
@@ -160,7 +175,7 @@ def test_k_zero_writes_zeros_and_empty_is_noop():
 @pytest.mark.parametrize("vname", VARIANTS)
 def test_batched_small(vname):
     v = pkg.variants()[vname]
-    b, M, N, K = 3, 160, 192, 192
+    b, M, N, K = (3, 64, 256, 2048) if vname.startswith("skinny") else (3, 160, 192, 192)
     say(f"[batched] {vname}")
     A = inputs.uniform((b, M, K), 7001, lo=-0.5, hi=0.5)
     B = inputs.uniform((b, K, N), 7002, lo=-0.5, hi=0.5)
