@@ -49,7 +49,7 @@ const char* const kVariantNames[] = {
     "pipelined_256x256x32_s4",
     "pipelined_256x256x32_s5",
     "pipelined_128x128x32_s4",
-    "skinny_64x32_w8_k32_s4",
+    "skinny_64x32_w4_k64_s4",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
@@ -87,8 +87,9 @@ bool pipelined_ok(const Call& c, int BK, int STAGES) {
     return true;
 }
 
-// the skinny kernel: 8 waves split K, 32-deep chunks, 4 B stages per wave
-constexpr int kSkWaves = 8, kSkChunk = 32, kSkStages = 4;
+// the skinny kernel: 4 waves split K, 64-deep chunks, 4 B stages and 3 A
+// slots per wave (the fastest of the measured ring shapes on 64 x 8192 x 8192)
+constexpr int kSkWaves = 4, kSkChunk = 64, kSkStages = 4, kSkSlots = 3;
 
 bool skinny_ok(const Call& c) {
     if (c.K <= 0 || c.K % (kSkWaves * kSkChunk) != 0) return false;
@@ -150,7 +151,7 @@ hipError_t launch_skinny(const Call& c, hipStream_t stream) {
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;
         a.B = static_cast<const T*>(c.B) + b0 * c.sB;
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
-        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSkWaves, kSkChunk, kSkStages, OutT>),
+        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSkWaves, kSkChunk, kSkStages, kSkSlots, OutT>),
                            dim3((unsigned)a.tiles_n, (unsigned)tm, (unsigned)nb), dim3(kSkWaves * 64), 0, stream, a);
     }
     return hipGetLastError();

@@ -3,17 +3,19 @@
 //
 // Such a product is bound by streaming B (K x N) from HBM once; A is small and
 // stays in L2.  To keep all 256 CUs streaming, a workgroup owns a 64 x 32
-// output block over ALL of K (N/32 workgroups), and its 8 waves split K into
-// 8 slices ("split-K inside the workgroup").  Each wave streams its slice
-// through private LDS rings -- a 4-stage ring for B chunks and a 2-slot ring
-// for A chunks -- filled by LDS-DMA, so the loop needs no workgroup barrier:
+// output block over ALL of K (N/32 workgroups), and its WAVES waves split K
+// into WAVES slices ("split-K inside the workgroup").  Each wave streams its slice
+// through private LDS rings -- SB stages for B chunks and SA slots for A
+// chunks -- filled by LDS-DMA, so the loop needs no workgroup barrier:
 // a stage is published to the only wave that reads it by that wave's own
 // vmcnt wait (the "bytes pending" half of the mbarrier page's completion
 // rule; nobody else has to arrive).  Everything asynchronous lands in LDS,
 // never in registers, so no copy of an in-flight register can be made.  At
-// the end the 8 partial 64 x 32 tiles are summed through LDS in a fixed wave
+// the end the WAVES partial 64 x 32 tiles are summed through LDS in a fixed wave
 // order (deterministic, no atomics, no workspace), converted and stored.
 #pragma once
+#include <utility>
+
 #include "device_common.hpp"
 #include "gemm_pipelined.hpp"   // swz_a
 
@@ -35,27 +37,80 @@ __device__ inline void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <typename T, int WAVES, int KC, int SB, typename OutT>
+template <typename T, int WAVES, int KC, int SB, int SA, typename OutT>
 struct SkinnyGemm {
-    static_assert(KC == 32, "A rows of 64 bytes (the 32-wide swizzle)");
-    static_assert(SB >= 3, "B runs at least two chunks ahead of A");
+    static_assert(KC == 32 || KC == 64, "A swizzles exist for 64- and 128-byte rows");
+    static_assert(SA >= 2 && SA - 1 <= SB - 2, "A runs PA = SA-1 chunks ahead, B at least one further");
     static constexpr int BM = 64, BN = 32;          // two 32x32 MFMA blocks
+    static constexpr int PA = SA - 1;               // A prefetch distance (chunks)
     static constexpr int KSTEPS = KC / 16;          // MFMA k-steps per chunk
-    static constexpr int A_BYTES = BM * KC * 2;     // 4 KiB per A chunk
-    static constexpr int B_BYTES = KC * BN * 2;     // 2 KiB per B chunk
+    static constexpr int A_BYTES = BM * KC * 2;     // one A chunk
+    static constexpr int B_BYTES = KC * BN * 2;     // one B chunk
     static constexpr int LA = A_BYTES / 1024;       // copies per A chunk
     static constexpr int LB = B_BYTES / 1024;       // copies per B chunk
-    static constexpr int WAVE_LDS = 2 * A_BYTES + SB * B_BYTES;
+    static constexpr int A_CHUNKS = KC / 8;         // 16-byte pieces per A row
+    static constexpr int A_ROWS_PER_INST = 64 / A_CHUNKS;
+    static constexpr int WAVE_LDS = SA * A_BYTES + SB * B_BYTES;
     static constexpr int RING_BYTES = WAVES * WAVE_LDS;
     static constexpr int RED_BYTES = WAVES * BM * BN * 4;
     static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // Issue order per chunk x is A(x+PA) (if it exists) then B(x+SB-1) (if it
+    // exists).  Chunk c needs A(c) and the older B(c); A(c) came from chunk
+    // c-PA.  vmcnt allowed at the top of chunk c = the copies issued after
+    // A(c).  Steady state: B of chunk c-PA plus PA-1 full chunks.
+    static constexpr int VM_STEADY = LB + (PA - 1) * (LA + LB);
+    static_assert(VM_STEADY < 64, "vmcnt is 6 bits");
+    // drain chunk d (0 .. SB-2), d counted from the first chunk with no B to
+    // issue; x are chunk positions relative to it (negative = steady)
+    static constexpr int vm_drain(int d) {
+        int n = (d - PA < 0) ? LB : 0;              // the rest of chunk d-PA
+        for (int x = d - PA + 1; x <= d - 1; ++x) n += ((x + PA < SB - 1) ? LA : 0) + ((x < 0) ? LB : 0);
+        return n;
+    }
     typedef typename Mfma<T>::frag_t frag_t;
 };
 
-template <typename T, int WAVES, int KC, int SB, typename OutT>
+// Compile-time check of the wait counts above: replay the issue order of a
+// wave with nch chunks copy by copy and find, for every chunk, how many
+// copies were issued after the last copy that chunk needs.
+template <int SB, int PA, int LA, int LB, int VM_STEADY, int (*VM_DRAIN)(int)>
+constexpr bool skinny_waits_match(int nch) {
+    int kind[4096] = {}, chunk[4096] = {}, n = 0;        // issue log (kind 0 = A, 1 = B)
+    auto push = [&](int k, int c, int cnt) {
+        for (int i = 0; i < cnt; ++i) { kind[n] = k; chunk[n] = c; ++n; }
+    };
+    auto allowed = [&](int c) {                           // copies after the last one chunk c needs
+        int last = -1;
+        for (int i = 0; i < n; ++i)
+            if (chunk[i] == c) last = i;
+        return n - 1 - last;
+    };
+    for (int x = -(SB - 1); x < 0; ++x) {
+        if (x + PA >= 0) push(0, x + PA, LA);
+        push(1, x + SB - 1, LB);
+    }
+    int c = 0;
+    for (; c + SB - 1 < nch; ++c) {
+        if (allowed(c) != VM_STEADY) return false;
+        push(0, c + PA, LA);
+        push(1, c + SB - 1, LB);
+    }
+    for (int d = 0; d < SB - 1; ++d) {
+        if (allowed(c + d) != VM_DRAIN(d)) return false;
+        if (c + d + PA < nch) push(0, c + d + PA, LA);
+    }
+    return true;
+}
+
+template <typename T, int WAVES, int KC, int SB, int SA, typename OutT>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs args) {
-    typedef SkinnyGemm<T, WAVES, KC, SB, OutT> G;
+    typedef SkinnyGemm<T, WAVES, KC, SB, SA, OutT> G;
+    constexpr int PA = G::PA;
+    static_assert(skinny_waits_match<SB, PA, G::LA, G::LB, G::VM_STEADY, &G::vm_drain>(SB) &&
+                      skinny_waits_match<SB, PA, G::LA, G::LB, G::VM_STEADY, &G::vm_drain>(SB + 1) &&
+                      skinny_waits_match<SB, PA, G::LA, G::LB, G::VM_STEADY, &G::vm_drain>(SB + 5),
+                  "vmcnt counts disagree with the replayed issue order");
     typedef typename G::frag_t frag_t;
     constexpr int BN = G::BN;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
@@ -84,14 +139,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
     const int kbase = wave * kw;
     const int nchunks = kw / KC;                    // host: kw % KC == 0, nchunks >= SB
 
-    // A copies: chunk rows m (64 bytes each), 16 rows per KiB; lane p brings
-    // row 16i + p/4 and lands at 16-byte slot p%4 of it; the global chunk it
-    // fetches is swizzled.  Rows >= M start past num_records and read zeros.
+    // A copies: chunk rows m (KC halves each); lane p of copy i brings row
+    // i*A_ROWS_PER_INST + p/A_CHUNKS and lands at 16-byte slot p%A_CHUNKS of
+    // it; the global piece it fetches is swizzled.  Rows >= M start past
+    // num_records and read zeros.
     uint32_t voffA[G::LA];
 #pragma unroll
     for (int i = 0; i < G::LA; ++i) {
-        const int row = 16 * i + lane / 4;
-        const int chunk = (lane % 4) ^ swz_a<32>(row);
+        const int row = G::A_ROWS_PER_INST * i + lane / G::A_CHUNKS;
+        const int chunk = (lane % G::A_CHUNKS) ^ swz_a<KC>(row);
         voffA[i] = (uint32_t)(((m0 + row) * lda + kbase + chunk * 8) * 2);
     }
     // B copies: chunk rows k (64 bytes = the 32 columns), 16 rows per KiB.
@@ -107,17 +163,17 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
     const uint32_t astep = KC * 2;                  // bytes per chunk along K
     const uint32_t bstep = (uint32_t)KC * ldb * 2;
 
-    // this wave's LDS: A slots [0, 2*A_BYTES), then B stages
+    // this wave's LDS: A slots [0, SA*A_BYTES), then B stages
     const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * G::WAVE_LDS;
     BPT_LDS char* wlds_p = lds + wave * G::WAVE_LDS;
 
     auto issue_a = [&](int c) __attribute__((always_inline)) {
-        const uint32_t dst = wlds + (c & 1) * G::A_BYTES;
+        const uint32_t dst = wlds + (c % SA) * G::A_BYTES;
 #pragma unroll
         for (int i = 0; i < G::LA; ++i) dma16(rsA, dst + i * 1024, voffA[i], c * astep);
     };
     auto issue_b = [&](int c) __attribute__((always_inline)) {
-        const uint32_t dst = wlds + 2 * G::A_BYTES + (c % SB) * G::B_BYTES;
+        const uint32_t dst = wlds + SA * G::A_BYTES + (c % SB) * G::B_BYTES;
 #pragma unroll
         for (int i = 0; i < G::LB; ++i) dma16(rsB, dst + i * 1024, voffB[i], c * bstep);
     };
@@ -129,7 +185,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
 #pragma unroll
     for (int kk = 0; kk < G::KSTEPS; ++kk) {
         const int row = lane % 32;                  // + mb*32 keeps the swizzle
-        rdA[kk] = (uint32_t)(row * KC * 2 + (((kk * 2 + lane / 32) ^ swz_a<32>(row)) * 16));
+        rdA[kk] = (uint32_t)(row * KC * 2 + (((kk * 2 + lane / 32) ^ swz_a<KC>(row)) * 16));
     }
     const int g = lane / 16, j = lane % 16;
     const uint32_t rdB = (uint32_t)((8 * (g / 2) + j / 4) * BN * 2 + (16 * (g % 2) + 4 * (j % 4)) * 2);
@@ -140,8 +196,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
         acc[mb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int c) __attribute__((always_inline)) {
-        BPT_LDS char* ap = wlds_p + (c & 1) * G::A_BYTES;
-        BPT_LDS char* bp = wlds_p + 2 * G::A_BYTES + (c % SB) * G::B_BYTES;
+        BPT_LDS char* ap = wlds_p + (c % SA) * G::A_BYTES;
+        BPT_LDS char* bp = wlds_p + SA * G::A_BYTES + (c % SB) * G::B_BYTES;
 #pragma unroll
         for (int kk = 0; kk < G::KSTEPS; ++kk) {
             BPT_LDS char* p = bp + rdB + kk * 16 * BN * 2;
@@ -156,42 +212,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
         }
     };
 
-    // Chunk c: B in stage c % SB, A in slot c % 2.  Issue order per chunk is
-    // A(c+1) then B(c+SB-1), so at the top of chunk c, after A(c) (issued one
-    // chunk earlier) only B(c+SB-2) was issued: vmcnt(LB) covers A(c) and
-    // the older B(c).  The stage and slot refilled in chunk c are those of
-    // chunk c-1, whose reads the lgkmcnt(0) wait has retired.
+    // Chunk c: B in stage c % SB, A in slot c % SA.  Chunk c waits for its
+    // copies (vmcnt counts, see SkinnyGemm), retires its own reads of chunk
+    // c-1 (lgkmcnt(0)) -- whose slot and stage are refilled next -- issues
+    // A(c+PA) and B(c+SB-1), then computes.
     //
-    // prologue = the pattern of chunks -(SB-1) .. -1: B(0 .. SB-3), A(0), B(SB-2)
+    // prologue = the pattern of chunks -(SB-1) .. -1
 #pragma unroll
-    for (int i = 0; i < SB - 2; ++i) issue_b(i);
-    issue_a(0);
-    issue_b(SB - 2);
+    for (int x = -(SB - 1); x < 0; ++x) {
+        if (x + PA >= 0) issue_a(x + PA);
+        issue_b(x + SB - 1);
+    }
 
     int c = 0;
     for (; c + SB - 1 < nchunks; ++c) {             // steady: both copies exist
-        wait_vm<G::LB>();
+        wait_vm<G::VM_STEADY>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue_a(c + 1);
+        issue_a(c + PA);
         issue_b(c + SB - 1);
         compute(c);
     }
-    // drain, the last SB-1 chunks: no B left to issue.  The first of them
-    // still had B(nchunks-1) issued after its A; after that, A(c) is the
-    // newest copy, so the wait is for everything.
-    wait_vm<G::LB>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue_a(c + 1);
-    compute(c);
-    ++c;
-#pragma unroll
-    for (int d = 1; d < SB - 1; ++d) {
-        wait_vm<0>();
+    // drain, the last SB-1 chunks: no B left to issue, A while it exists
+    auto drain_step = [&]<int D>() __attribute__((always_inline)) {
+        wait_vm<G::vm_drain(D)>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (d + 1 < SB - 1) issue_a(c + 1);         // static: d is unrolled
-        compute(c);
-        ++c;
-    }
+        if constexpr (D + PA < SB - 1) issue_a(c + D + PA);
+        compute(c + D);
+    };
+    [&]<int... D>(std::integer_sequence<int, D...>) {
+        (drain_step.template operator()<D>(), ...);
+    }(std::make_integer_sequence<int, SB - 1>{});
 
     // ---- reduction of the WAVES partial tiles, fixed order ------------------
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");

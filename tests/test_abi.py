@@ -135,10 +135,10 @@ def test_automatic_variant_choice():
     # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
     # few rows of A: the K-split skinny kernel
-    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == v["skinny_64x32_w8_k32_s4"]
-    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == v["skinny_64x32_w8_k32_s4"]
+    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == v["skinny_64x32_w4_k64_s4"]
+    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == v["skinny_64x32_w4_k64_s4"]
     # ... unless K is too short for its 8 waves x 4 chunks of 32
-    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) != v["skinny_64x32_w8_k32_s4"]
+    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) != v["skinny_64x32_w4_k64_s4"]
     # N % 8 != 0: column chunks would straddle N, so only the guarded kernel
     assert pkg.select_variant("f16", 1, 64, 8190, 8192, 8192, 8192) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 4096, 4092, 4096, 4096, 4096) == v["generic_64x64x16"]

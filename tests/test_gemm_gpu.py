@@ -66,7 +66,7 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
             "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
-            "skinny_64x32_w8_k32_s4"]
+            "skinny_64x32_w4_k64_s4"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
 # least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
 # aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
@@ -76,10 +76,10 @@ SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 192), (1, 8, 256), (
 SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64), (96, 201, 256)]
 
 
-# the skinny variant splits K over 8 waves in 32-deep chunks, 4 per wave at
+# the skinny variant splits K over 4 waves in 64-deep chunks, 4 per wave at
 # least: K a multiple of 256 and >= 1024; any M (64-row tiles); N % 8 == 0 with
-# a ragged last 32-column tile; chunk counts per wave both below, at and above
-# the ring depth so stages are reused
+# a ragged last 32-column tile; chunk counts per wave at the ring depth (K =
+# 1024) and above it so stages are reused
 SHAPES_SKINNY = [(64, 1024, 2048), (37, 320, 2560), (100, 256, 2048), (1, 512, 4096), (64, 2048, 3072),
                  (64, 200, 1024), (70, 264, 1280), (64, 256, 8192)]
 
