@@ -7,7 +7,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "../../include/bpt_gemm.h"
 #include "gemm_generic.hpp"
@@ -37,8 +40,9 @@ enum Variant {
     V_PIPE_256_K32_S4 = 4,  // 256x256 tile, BK 32, 4 stages
     V_PIPE_256_K32_S5 = 5,  // 256x256 tile, BK 32, 5 stages
     V_PIPE_128_K32_S4 = 6,  // 128x128 tile, BK 32, 4 stages
-    V_SKINNY = 7,           // 64x32 tile over all of K, 8 waves split K, per-wave LDS rings
-    V_COUNT = 7
+    V_SKINNY = 7,           // 64x32 block over all of K, 4 waves split K, per-wave LDS rings
+    V_SKINNY_WIDE = 8,      // 64x128 block, K also split over workgroups, + split-sum kernel
+    V_COUNT = 8
 };
 
 const char* const kVariantNames[] = {
@@ -50,11 +54,12 @@ const char* const kVariantNames[] = {
     "pipelined_256x256x32_s5",
     "pipelined_128x128x32_s4",
     "skinny_64x32_w4_k64_s4",
+    "skinny_64x128_w4_k32_s4_splitk",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0};
 
 
 struct Call {
@@ -91,9 +96,8 @@ bool pipelined_ok(const Call& c, int BK, int STAGES) {
 // slots per wave (the fastest of the measured ring shapes on 64 x 8192 x 8192)
 constexpr int kSkWaves = 4, kSkChunk = 64, kSkStages = 4, kSkSlots = 3;
 
-bool skinny_ok(const Call& c) {
-    if (c.K <= 0 || c.K % (kSkWaves * kSkChunk) != 0) return false;
-    if (c.K / (kSkWaves * kSkChunk) < kSkStages) return false;
+// operand requirements shared by both skinny kernels
+bool skinny_operands_ok(const Call& c) {
     if (c.N % 8 != 0) return false;
     if (!aligned16(c.A) || !aligned16(c.B)) return false;
     if (c.lda % 8 != 0 || c.ldb % 8 != 0 || c.sA % 8 != 0 || c.sB % 8 != 0) return false;
@@ -102,11 +106,87 @@ bool skinny_ok(const Call& c) {
     return extA <= kI31 && extB <= kI31;
 }
 
+bool skinny_ok(const Call& c) {
+    if (c.K <= 0 || c.K % (kSkWaves * kSkChunk) != 0) return false;
+    if (c.K / (kSkWaves * kSkChunk) < kSkStages) return false;
+    return skinny_operands_ok(c);
+}
+
+// the wide skinny kernel: 128-column blocks (256-byte B row pieces), 4 waves,
+// 32-deep chunks, 4 B stages and 2 A slots per wave, K split over `splits`
+// workgroups per block
+constexpr int kSwWaves = 4, kSwChunk = 32, kSwStages = 4, kSwSlots = 2, kSwBN = 128;
+constexpr long long kWorkspaceMax = 256LL << 20;   // bytes per (device, stream)
+
+long long wide_blocks_per_launch(const Call& c) {
+    long long nb = c.batch < 65535 ? c.batch : 65535;
+    return (c.N + kSwBN - 1) / kSwBN * ((c.M + 63) / 64) * nb;
+}
+
+bool wide_split_fits(const Call& c, int S) {
+    const long long per = (long long)S * kSwWaves * kSwChunk;
+    return c.K % per == 0 && c.K / per >= kSwStages;
+}
+
+// Splits for the wide kernel: the fewest that give one workgroup per CU
+// (256), else the most that K allows, within the workspace limit; 0 when
+// the kernel cannot take the call.
+int wide_splits(const Call& c) {
+    if (c.K <= 0 || !skinny_operands_ok(c) || !wide_split_fits(c, 1)) return 0;
+    const long long blocks = wide_blocks_per_launch(c);
+    int best = 1;
+    for (int S = 2; S <= 8; S *= 2) {
+        if (!wide_split_fits(c, S)) break;
+        if (blocks * S * 64 * kSwBN * 4 > kWorkspaceMax) break;
+        if (blocks * best >= 256) break;
+        best = S;
+    }
+    return best;
+}
+
+// One device workspace per (device, stream), grown on demand and kept until
+// the process ends; nullptr when it cannot be had (allocation failure, or the
+// stream is being captured, where allocating is not allowed).
+float* stream_workspace(long long bytes, hipStream_t stream) {
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, std::pair<void*, long long>> spaces;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto& w = spaces[{dev, stream}];
+    if (w.second >= bytes) return static_cast<float*>(w.first);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) (void)hipGetLastError();
+    if (cap != hipStreamCaptureStatusNone) return nullptr;
+    long long want = bytes > 2 * w.second ? bytes : 2 * w.second;
+    if (want > kWorkspaceMax) want = bytes;
+    void* p = nullptr;
+    if (hipMalloc(&p, (size_t)want) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (w.first != nullptr) {
+        // the old workspace is only ever used on this stream
+        (void)hipStreamSynchronize(stream);
+        (void)hipFree(w.first);
+    }
+    w = {p, want};
+    return static_cast<float*>(p);
+}
+
 int choose(const Call& c) {
     long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
-    // few rows of A: stream B once with the K-split skinny kernel when that
-    // yields at least half a workgroup per CU
-    if (c.M <= 64 && (c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
+    // few rows of A: stream B once with a skinny kernel when that yields at
+    // least half a workgroup per CU; the wide one reads B in 256-byte row
+    // pieces, which stream faster than the narrow one's 64-byte pieces
+    if (c.M <= 64) {
+        const int S = wide_splits(c);
+        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_WIDE;
+        if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
+    }
     const bool big = tiles256 >= 128;
     if (big && pipelined_ok(c, 32, 4)) return V_PIPE_256_K32_S4;
     if (pipelined_ok(c, 32, 4)) return V_PIPE_128_K32_S4;
@@ -145,14 +225,63 @@ hipError_t launch_skinny(const Call& c, hipStream_t stream) {
     a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
     a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
     a.tiles_n = (int)((c.N + 31) / 32);
+    a.splits = 1;
+    a.partial = nullptr;
     const long long tm = (c.M + 63) / 64;
     for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
         long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;
         a.B = static_cast<const T*>(c.B) + b0 * c.sB;
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
-        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSkWaves, kSkChunk, kSkStages, kSkSlots, OutT>),
+        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSkWaves, kSkChunk, kSkStages, kSkSlots, 1, OutT>),
                            dim3((unsigned)a.tiles_n, (unsigned)tm, (unsigned)nb), dim3(kSkWaves * 64), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename OutT>
+void launch_split_sum(const bpt::SkinnySumArgs& a, int S, hipStream_t stream) {
+    const long long threads = a.blocks * 64 * kSwBN / 4;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (S == 2) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 2, OutT>), grid, dim3(256), 0, stream, a);
+    else if (S == 4) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 4, OutT>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 8, OutT>), grid, dim3(256), 0, stream, a);
+}
+
+template <typename T, typename OutT>
+hipError_t launch_skinny_wide(const Call& c, hipStream_t stream) {
+    int S = wide_splits(c);
+    float* ws = nullptr;
+    if (S > 1) {
+        ws = stream_workspace(wide_blocks_per_launch(c) * S * 64 * kSwBN * 4, stream);
+        if (ws == nullptr) S = 1;       // S > 1 fits K, so S = 1 does too
+    }
+    bpt::SkinnyArgs a;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_n = (int)((c.N + kSwBN - 1) / kSwBN);
+    a.splits = S;
+    a.partial = ws;
+    const long long tm = (c.M + 63) / 64;
+    bpt::SkinnySumArgs r;
+    r.partial = ws;
+    r.M = (int)c.M; r.N = (int)c.N; r.ldc = (int)c.ldc;
+    r.strideC = c.sC;
+    r.tiles_n = a.tiles_n; r.tiles_m = (int)tm;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        a.A = static_cast<const T*>(c.A) + b0 * c.sA;
+        a.B = static_cast<const T*>(c.B) + b0 * c.sB;
+        a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
+        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSwWaves, kSwChunk, kSwStages, kSwSlots, 4, OutT>),
+                           dim3((unsigned)(a.tiles_n * S), (unsigned)tm, (unsigned)nb), dim3(kSwWaves * 64), 0,
+                           stream, a);
+        if (S > 1) {
+            r.C = a.C;
+            r.blocks = a.tiles_n * tm * nb;
+            launch_split_sum<OutT>(r, S, stream);
+        }
     }
     return hipGetLastError();
 }
@@ -199,6 +328,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PIPE_256_K32_S5: return launch_pipelined<T, OutT, 256, 256, 32, 5>(c, stream);
         case V_PIPE_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4>(c, stream);
         case V_SKINNY: return launch_skinny<T, OutT>(c, stream);
+        case V_SKINNY_WIDE: return launch_skinny_wide<T, OutT>(c, stream);
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -227,8 +357,9 @@ bool variant_accepts(const Call& c, int v) {
     switch (v) {
         case V_GENERIC: return true;
         case V_SKINNY: return skinny_ok(c);
+        case V_SKINNY_WIDE: return wide_splits(c) > 0;
         default:
-            if (v > V_GENERIC && v <= V_COUNT) return pipelined_ok(c, kVariantBK[v], kVariantStages[v]);
+            if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v]);
             return false;
     }
 }

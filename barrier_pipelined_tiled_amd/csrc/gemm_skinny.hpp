@@ -2,17 +2,26 @@
 // shapes, e.g. 64 x 8192 x 8192): C (M x N) = A (M x K) * B (K x N).
 //
 // Such a product is bound by streaming B (K x N) from HBM once; A is small and
-// stays in L2.  To keep all 256 CUs streaming, a workgroup owns a 64 x 32
-// output block over ALL of K (N/32 workgroups), and its WAVES waves split K
-// into WAVES slices ("split-K inside the workgroup").  Each wave streams its slice
-// through private LDS rings -- SB stages for B chunks and SA slots for A
-// chunks -- filled by LDS-DMA, so the loop needs no workgroup barrier:
-// a stage is published to the only wave that reads it by that wave's own
-// vmcnt wait (the "bytes pending" half of the mbarrier page's completion
-// rule; nobody else has to arrive).  Everything asynchronous lands in LDS,
-// never in registers, so no copy of an in-flight register can be made.  At
-// the end the WAVES partial 64 x 32 tiles are summed through LDS in a fixed wave
-// order (deterministic, no atomics, no workspace), converted and stored.
+// stays in L2.  A workgroup owns a 64 x BN output block (BN = 32 NB columns)
+// over a range of K, and its waves split that range once more ("split-K
+// inside the workgroup").  Each wave streams its share through private LDS
+// rings -- SB stages for B chunks and SA slots for A chunks -- filled by
+// LDS-DMA, so the loop needs no workgroup barrier: a stage is published to the
+// only wave that reads it by that wave's own vmcnt wait (the "bytes pending"
+// half of the mbarrier page's completion rule; nobody else has to arrive).
+// Everything asynchronous lands in LDS, never in registers, so no copy of an
+// in-flight register can be made.  The wave partials are summed through LDS
+// in a fixed wave order.
+//
+// HBM streams best when each workgroup reads wide pieces of a B row (a
+// 256-byte piece reads at about 1.4x the rate of a 64-byte one), but a 128-
+// column block leaves too few workgroups to occupy every CU on most shapes.
+// So K may also be split across `splits` workgroups per block: each writes
+// its fp32 partial block to a workspace, and a second, small kernel adds the
+// `splits` partials of every block in split order (deterministic), converts
+// and stores C.  The kernel boundary orders the two; a release/acquire pair
+// inside one kernel would cost an L2 write-back per workgroup, several times
+// the cost of the extra launch.
 #pragma once
 #include <utility>
 
@@ -28,7 +37,9 @@ struct SkinnyArgs {
     int M, N, K;
     int lda, ldb, ldc;
     long long strideA, strideB, strideC;
-    int tiles_n;
+    int tiles_n;            // column blocks of BN
+    int splits;             // workgroups per block along K (1: no workspace)
+    float* partial;         // splits > 1: [block][split][64][BN] fp32
 };
 
 template <int N>
@@ -37,11 +48,12 @@ __device__ inline void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <typename T, int WAVES, int KC, int SB, int SA, typename OutT>
+template <typename T, int WAVES, int KC, int SB, int SA, int NB, typename OutT>
 struct SkinnyGemm {
     static_assert(KC == 32 || KC == 64, "A swizzles exist for 64- and 128-byte rows");
     static_assert(SA >= 2 && SA - 1 <= SB - 2, "A runs PA = SA-1 chunks ahead, B at least one further");
-    static constexpr int BM = 64, BN = 32;          // two 32x32 MFMA blocks
+    static_assert(NB == 1 || NB == 4, "B layouts exist for 64- and 256-byte rows");
+    static constexpr int BM = 64, BN = 32 * NB;     // 2 x NB blocks of 32x32
     static constexpr int PA = SA - 1;               // A prefetch distance (chunks)
     static constexpr int KSTEPS = KC / 16;          // MFMA k-steps per chunk
     static constexpr int A_BYTES = BM * KC * 2;     // one A chunk
@@ -50,9 +62,15 @@ struct SkinnyGemm {
     static constexpr int LB = B_BYTES / 1024;       // copies per B chunk
     static constexpr int A_CHUNKS = KC / 8;         // 16-byte pieces per A row
     static constexpr int A_ROWS_PER_INST = 64 / A_CHUNKS;
+    static constexpr int B_PIECES = BN / 8;         // 16-byte pieces per B row
+    static constexpr int B_ROWS_PER_INST = 64 / B_PIECES;
     static constexpr int WAVE_LDS = SA * A_BYTES + SB * B_BYTES;
     static constexpr int RING_BYTES = WAVES * WAVE_LDS;
-    static constexpr int RED_BYTES = WAVES * BM * BN * 4;
+    // wave partials in LDS, rows padded by 16 bytes: the 32 rows one store
+    // instruction writes then fall on different banks
+    static constexpr int RED_PITCH = BN * 4 + 16;
+    static constexpr int RED_WAVE = BM * RED_PITCH;
+    static constexpr int RED_BYTES = WAVES * RED_WAVE;
     static constexpr int LDS_BYTES = RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     // Issue order per chunk x is A(x+PA) (if it exists) then B(x+SB-1) (if it
@@ -103,9 +121,19 @@ constexpr bool skinny_waits_match(int nch) {
     return true;
 }
 
-template <typename T, int WAVES, int KC, int SB, int SA, typename OutT>
+// B rows of a 128-column block (16 pieces of 16 bytes): piece p of k row k
+// sits at p ^ swz_b(k), the layout of the pipelined kernel's B tiles, which
+// keeps both the copies and the transposed fragment reads conflict-free.
+// 32-column rows (4 pieces) need none: 4 rows fill the 64 banks.
+template <int NB>
+__device__ inline int skinny_swz_b(int k) {
+    if constexpr (NB == 4) return swz_b(k);
+    return 0;
+}
+
+template <typename T, int WAVES, int KC, int SB, int SA, int NB, typename OutT>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs args) {
-    typedef SkinnyGemm<T, WAVES, KC, SB, SA, OutT> G;
+    typedef SkinnyGemm<T, WAVES, KC, SB, SA, NB, OutT> G;
     constexpr int PA = G::PA;
     static_assert(skinny_waits_match<SB, PA, G::LA, G::LB, G::VM_STEADY, &G::vm_drain>(SB) &&
                       skinny_waits_match<SB, PA, G::LA, G::LB, G::VM_STEADY, &G::vm_drain>(SB + 1) &&
@@ -113,19 +141,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
                   "vmcnt counts disagree with the replayed issue order");
     typedef typename G::frag_t frag_t;
     constexpr int BN = G::BN;
+    constexpr int BLOCK = G::BM * BN;               // outputs per block
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
     BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int splits = args.splits;
 
-    // XCD-aware order: consecutive column tiles on the same XCD share L2
-    // lines of B (a 32-column tile reads 64 bytes of each 128-byte line).
+    // XCD-aware order: a run of consecutive workgroups -- neighbouring column
+    // blocks with all their splits -- stays on one XCD, so neighbouring B
+    // pieces share one L2.
     int pid = blockIdx.x;
     const int num = gridDim.x;
     if ((num & 7) == 0) pid = (pid & 7) * (num >> 3) + (pid >> 3);
-    const int n0 = pid * BN;
+    const int tile = pid / splits, split = pid - tile * splits;
+    const int n0 = tile * BN;
     const int m0 = blockIdx.y * G::BM;
     const int batch = blockIdx.z;
 
@@ -135,9 +167,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
     const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
     const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + N) * 2));
 
-    const int kw = K / WAVES;                       // this wave's K slice
-    const int kbase = wave * kw;
-    const int nchunks = kw / KC;                    // host: kw % KC == 0, nchunks >= SB
+    // this workgroup's K range, and this wave's chunks in it, interleaved:
+    // chunk c of wave w is chunk c*WAVES + w of the range, so the waves of a
+    // workgroup read neighbouring rows of B at about the same time
+    const int kwg = K / splits;                     // host: kwg % (WAVES*KC) == 0
+    const int nchunks = kwg / (WAVES * KC);         // host: nchunks >= SB
+    const int kbase = split * kwg + wave * KC;
 
     // A copies: chunk rows m (KC halves each); lane p of copy i brings row
     // i*A_ROWS_PER_INST + p/A_CHUNKS and lands at 16-byte slot p%A_CHUNKS of
@@ -150,18 +185,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
         const int chunk = (lane % G::A_CHUNKS) ^ swz_a<KC>(row);
         voffA[i] = (uint32_t)(((m0 + row) * lda + kbase + chunk * 8) * 2);
     }
-    // B copies: chunk rows k (64 bytes = the 32 columns), 16 rows per KiB.
-    // A lane whose 8 columns start at or past N fetches the last in-bounds
-    // chunk instead (host: N % 8 == 0); those columns are never stored.
+    // B copies: chunk rows k of BN columns; lane p of copy i brings row
+    // i*B_ROWS_PER_INST + p/B_PIECES into LDS piece p%B_PIECES of it, which
+    // holds global piece (p%B_PIECES) ^ swz(k).  A lane whose 8 columns start
+    // at or past N fetches the last in-bounds piece instead (host: N % 8 ==
+    // 0); those columns are never stored.
     uint32_t voffB[G::LB];
 #pragma unroll
     for (int i = 0; i < G::LB; ++i) {
-        int col = n0 + 8 * (lane % 4);
+        const int row = G::B_ROWS_PER_INST * i + lane / G::B_PIECES;
+        int col = n0 + 8 * ((lane % G::B_PIECES) ^ skinny_swz_b<NB>(row));
         if (col >= N) col = N - 8;
-        voffB[i] = (uint32_t)(((kbase + 16 * i + lane / 4) * ldb + col) * 2);
+        voffB[i] = (uint32_t)(((kbase + row) * ldb + col) * 2);
     }
-    const uint32_t astep = KC * 2;                  // bytes per chunk along K
-    const uint32_t bstep = (uint32_t)KC * ldb * 2;
+    const uint32_t astep = WAVES * KC * 2;          // bytes per chunk along K
+    const uint32_t bstep = (uint32_t)WAVES * KC * ldb * 2;
 
     // this wave's LDS: A slots [0, SA*A_BYTES), then B stages
     const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * G::WAVE_LDS;
@@ -179,8 +217,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
     };
 
     // fragment reads.  A (row block mb, k-step kk): row mb*32 + l%32, chunk
-    // kk*2 + l/32, swizzled.  B: a 16-lane group g reads rows kk*16 + 8*(g/2)
-    // + 4h + j/4, columns 16*(g%2) + 4*(j%4) (j = l%16), transposed.
+    // kk*2 + l/32, swizzled.  B block nb: a 16-lane group g reads rows kk*16 +
+    // 8*(g/2) + 4h + j/4 and columns nb*32 + 16*(g%2) + 4*(j%4) (j = l%16),
+    // transposed, i.e. logical piece 4nb + 2(g%2) + (j%4)/2, half (j%2); the
+    // row's low two bits are j/4 for every kk and h, so is its swizzle.
     uint32_t rdA[G::KSTEPS];
 #pragma unroll
     for (int kk = 0; kk < G::KSTEPS; ++kk) {
@@ -188,26 +228,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
         rdA[kk] = (uint32_t)(row * KC * 2 + (((kk * 2 + lane / 32) ^ swz_a<KC>(row)) * 16));
     }
     const int g = lane / 16, j = lane % 16;
-    const uint32_t rdB = (uint32_t)((8 * (g / 2) + j / 4) * BN * 2 + (16 * (g % 2) + 4 * (j % 4)) * 2);
+    uint32_t rdB[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int piece = (4 * nb + 2 * (g % 2) + (j % 4) / 2) ^ skinny_swz_b<NB>(j / 4);
+        rdB[nb] = (uint32_t)((8 * (g / 2) + j / 4) * BN * 2 + piece * 16 + (j % 2) * 8);
+    }
 
-    float16_t acc[2];
+    float16_t acc[2][NB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
-        acc[mb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int c) __attribute__((always_inline)) {
         BPT_LDS char* ap = wlds_p + (c % SA) * G::A_BYTES;
         BPT_LDS char* bp = wlds_p + SA * G::A_BYTES + (c % SB) * G::B_BYTES;
 #pragma unroll
         for (int kk = 0; kk < G::KSTEPS; ++kk) {
-            BPT_LDS char* p = bp + rdB + kk * 16 * BN * 2;
-            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
-            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
-            frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            frag_t a[2];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                frag_t a = *(BPT_LDS frag_t*)(ap + rdA[kk] + mb * 32 * KC * 2);
-                acc[mb] = Mfma<T>::mma32(b, a, acc[mb]);
+            for (int mb = 0; mb < 2; ++mb) a[mb] = *(BPT_LDS frag_t*)(ap + rdA[kk] + mb * 32 * KC * 2);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                BPT_LDS char* p = bp + rdB[nb] + kk * 16 * BN * 2;
+                short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+                short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
+                frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = Mfma<T>::mma32(b, a[mb], acc[mb][nb]);
             }
         }
     };
@@ -243,27 +293,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
         (drain_step.template operator()<D>(), ...);
     }(std::make_integer_sequence<int, SB - 1>{});
 
-    // ---- reduction of the WAVES partial tiles, fixed order ------------------
+    // ---- the WAVES partial blocks, summed in fixed order --------------------
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // partial of this wave, row-major [64][32] fp32 (lane's 4 consecutive
-    // columns per register group: the B-first MFMA layout)
-    BPT_LDS char* red = lds + wave * (G::BM * BN * 4);
+    // partial of this wave, row-major [64][BN] fp32 with RED_PITCH-byte rows
+    // (lane's 4 consecutive columns per register group: the B-first MFMA
+    // layout)
+    BPT_LDS char* red = lds + wave * G::RED_WAVE;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            float4_t v = {acc[mb][4 * gq], acc[mb][4 * gq + 1], acc[mb][4 * gq + 2], acc[mb][4 * gq + 3]};
-            const int r = mb * 32 + lane % 32, col = 8 * gq + 4 * (lane / 32);
-            *(BPT_LDS float4_t*)(red + (r * BN + col) * 4) = v;
-        }
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                float4_t v = {acc[mb][nb][4 * gq], acc[mb][nb][4 * gq + 1], acc[mb][nb][4 * gq + 2],
+                              acc[mb][nb][4 * gq + 3]};
+                const int r = mb * 32 + lane % 32, col = nb * 32 + 8 * gq + 4 * (lane / 32);
+                *(BPT_LDS float4_t*)(red + r * G::RED_PITCH + col * 4) = v;
+            }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
-    constexpr int OUTS = G::BM * BN;                // 2048 outputs, 4 per thread
-    for (int e = tid * 4; e < OUTS; e += WAVES * 64 * 4) {
+    auto store_c = [&](int e, float4_t s) __attribute__((always_inline)) {
         const int r = e / BN, col = e % BN;
-        float4_t s = *(BPT_LDS float4_t*)(lds + (r * BN + col) * 4);
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) s += *(BPT_LDS float4_t*)(lds + w * (G::BM * BN * 4) + (r * BN + col) * 4);
         const int grow = m0 + r, gcol = n0 + col;
         if (grow < M) {
             OutT* dst = Cb + (long long)grow * args.ldc + gcol;
@@ -271,7 +321,61 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
             for (int q = 0; q < 4; ++q)
                 if (gcol + q < N) dst[q] = cvt_out<OutT>(s[q]);
         }
+    };
+    constexpr int STEP = WAVES * 64 * 4;            // 4 outputs per thread per pass
+    auto wave_sum = [&](int e) __attribute__((always_inline)) {
+        BPT_LDS char* q = lds + (e / BN) * G::RED_PITCH + (e % BN) * 4;
+        float4_t s = *(BPT_LDS float4_t*)q;
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) s += *(BPT_LDS float4_t*)(q + w * G::RED_WAVE);
+        return s;
+    };
+    if (splits == 1) {
+        for (int e = tid * 4; e < BLOCK; e += STEP) store_c(e, wave_sum(e));
+        return;
     }
+
+    // ---- K split across workgroups: the partial goes to the workspace -------
+    const long long blk = ((long long)batch * gridDim.y + blockIdx.y) * args.tiles_n + tile;
+    float* part = args.partial + (blk * splits + split) * BLOCK;
+    for (int e = tid * 4; e < BLOCK; e += STEP) *(float4_t*)(part + e) = wave_sum(e);
+}
+
+struct SkinnySumArgs {
+    const float* partial;   // [block][split][64][BN] fp32, blocks ordered (batch, row block, column block)
+    void* C;
+    int M, N, ldc;
+    long long strideC;
+    int tiles_n, tiles_m;
+    long long blocks;       // blocks of this launch
+};
+
+// C block = sum over splits of the partial blocks, in split order.  One
+// thread per 4 consecutive outputs of a block row.
+template <int BN, int S, typename OutT>
+__global__ __launch_bounds__(256) void skinny_sum_kernel(SkinnySumArgs args) {
+    constexpr int BLOCK = 64 * BN;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long blk = gid / (BLOCK / 4);
+    if (blk >= args.blocks) return;
+    const int e = (int)(gid - blk * (BLOCK / 4)) * 4;
+    const float* p = args.partial + blk * S * BLOCK + e;
+    float4_t v[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) v[q] = *(const float4_t*)(p + q * BLOCK);
+    float4_t s = v[0];
+#pragma unroll
+    for (int q = 1; q < S; ++q) s += v[q];
+    const int tn = (int)(blk % args.tiles_n);
+    const long long rest = blk / args.tiles_n;
+    const int tm = (int)(rest % args.tiles_m);
+    const long long batch = rest / args.tiles_m;
+    const int row = tm * 64 + e / BN, col = tn * BN + e % BN;
+    if (row >= args.M) return;
+    OutT* dst = static_cast<OutT*>(args.C) + batch * args.strideC + (long long)row * args.ldc + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (col + q < args.N) dst[q] = cvt_out<OutT>(s[q]);
 }
 
 }  // namespace bpt

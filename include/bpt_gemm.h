@@ -20,13 +20,24 @@
  * reads bfloat16.  out_fp32 = 0 writes C in the input type (rounded to
  * nearest even from the fp32 sum); out_fp32 = 1 writes fp32.
  *
- * Ownership: A, B and C are DEVICE pointers owned by the caller; the library
- * allocates, frees and retains nothing per call and holds no per-call state.
- * C must not overlap A or B.
+ * Ownership: A, B and C are DEVICE pointers owned by the caller.  C must not
+ * overlap A or B.  The library keeps no per-call state; its one allocation is
+ * the workspace of the split-K path for few rows of A (variant
+ * skinny_64x128_w4_k32_s4_splitk when it splits K over workgroups): one
+ * device buffer per (device, stream), allocated with hipMalloc by the first
+ * call on that stream that needs it, replaced by a larger one when a later
+ * call needs more (that call synchronises the stream before freeing the old
+ * one), and kept until the process exits -- at most 256 MiB each.  Calls on
+ * one stream use it in stream order; calls on different streams never share
+ * one.  A call that cannot get it (the allocation fails, or the stream is
+ * being captured into a graph) runs the same kernel without splitting K,
+ * which needs no workspace.
  *
  * Execution: the call validates its arguments on the host, enqueues the
  * kernel(s) on `stream` (NULL = the default stream) and returns without
- * waiting.  Completion is observed by synchronising the stream.
+ * waiting.  Completion is observed by synchronising the stream.  The split-K
+ * path enqueues two kernels: the K-split products, then the in-order sum of
+ * their fp32 partials.
  *
  * Errors: nothing is launched unless the status is BPT_OK.
  *   BPT_ERR_INVALID_ARG  a size or stride is negative, a leading dimension is

@@ -134,11 +134,18 @@ def test_automatic_variant_choice():
     # K = 64 is one 64-wide tile (two stages need two) and two 32-wide tiles
     # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
-    # few rows of A: the K-split skinny kernel
-    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == v["skinny_64x32_w4_k64_s4"]
-    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == v["skinny_64x32_w4_k64_s4"]
-    # ... unless K is too short for its 8 waves x 4 chunks of 32
-    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) != v["skinny_64x32_w4_k64_s4"]
+    # few rows of A: the wide skinny kernel (128-column blocks, K split over
+    # 4 or 8 workgroups to reach one workgroup per CU) ...
+    wide, narrow = v["skinny_64x128_w4_k32_s4_splitk"], v["skinny_64x32_w4_k64_s4"]
+    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == wide
+    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == wide
+    assert pkg.select_variant("f16", 1, 1, 32768, 512, 512, 32768) == wide      # 256 blocks, no split
+    # ... the narrow one (32-column blocks over all of K) when K allows the
+    # wide one too few workgroups: 32 blocks x 2 splits, but 128 narrow ones
+    assert pkg.select_variant("f16", 1, 64, 4096, 1024, 1024, 4096) == narrow
+    # ... and neither when K is too short for either ring (8192 / 128 = 64
+    # wide blocks, K = 768 one split only; narrow needs K >= 1024)
+    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) not in (wide, narrow)
     # N % 8 != 0: column chunks would straddle N, so only the guarded kernel
     assert pkg.select_variant("f16", 1, 64, 8190, 8192, 8192, 8192) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 4096, 4092, 4096, 4096, 4096) == v["generic_64x64x16"]

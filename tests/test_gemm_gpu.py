@@ -66,7 +66,7 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
             "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
-            "skinny_64x32_w4_k64_s4"]
+            "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
 # least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
 # aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
@@ -82,9 +82,16 @@ SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64),
 # 1024) and above it so stages are reused
 SHAPES_SKINNY = [(64, 1024, 2048), (37, 320, 2560), (100, 256, 2048), (1, 512, 4096), (64, 2048, 3072),
                  (64, 200, 1024), (70, 264, 1280), (64, 256, 8192)]
+# the wide skinny variant: 128-column blocks, K split over S workgroups with
+# S*128 | K and K/(S*128) >= 4.  Above, S comes out as 4, 4, 4, 8, 4, 2, 2, 8
+# (the fewest splits reaching 256 workgroups, else the most that K allows);
+# these two allow S = 1 only (no workspace, no second kernel)
+SHAPES_WIDE_ONLY = [(64, 1024, 512), (3, 136, 640)]
 
 
 def _shapes(vname):
+    if vname.startswith("skinny_64x128"):
+        return SHAPES_SKINNY + SHAPES_WIDE_ONLY
     if vname.startswith("skinny"):
         return SHAPES_SKINNY
     return SHAPES_PIPE + (SHAPES_GENERIC_ONLY if vname.startswith("generic") else [])
@@ -206,6 +213,33 @@ def test_repeat_runs_bitwise_identical():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+def test_split_k_workspace_streams_and_growth():
+    """The split-K path keeps one workspace per stream: calls on two streams
+    in flight together, and a call that needs a larger workspace after a
+    smaller one, must each give the result of a lone call, bit for bit (the
+    split sums run in a fixed order)."""
+    v = pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
+    shapes = [(64, 256, 2048), (64, 2048, 4096), (32, 1024, 8192)]     # S = 4, 8, 8; growing
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A = inputs.uniform((M, K), 7201 + i, nonzero=True).to(DEV)
+        B = inputs.uniform((K, N), 7301 + i, nonzero=True).to(DEV)
+        data.append((A, B))
+    lone = [run(A.cpu(), B.cpu(), "f16", True, v) for A, B in data]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        for i, (A, B) in enumerate(data):
+            st = s1 if (i + rep) % 2 == 0 else s2
+            C = torch.empty((A.shape[0], B.shape[1]), dtype=torch.float32, device=DEV)
+            with torch.cuda.stream(st):
+                pkg.gemm_ex(A, B, C, out_fp32=True, variant=v, stream=st)
+            outs.append((i, C))
+    torch.cuda.synchronize()
+    for i, C in outs:
+        assert torch.equal(C.cpu(), lone[i]), i
 
 
 # ----------------------------------------------------------------------------
