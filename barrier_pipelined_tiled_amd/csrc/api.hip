@@ -241,7 +241,7 @@ hipError_t launch_skinny(const Call& c, hipStream_t stream) {
 
 template <typename OutT>
 void launch_split_sum(const bpt::SkinnySumArgs& a, int S, hipStream_t stream) {
-    const long long threads = a.blocks * 64 * kSwBN / 4;
+    const long long threads = a.blocks * 64 * kSwBN / 8;
     const dim3 grid((unsigned)((threads + 255) / 256));
     if (S == 2) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 2, OutT>), grid, dim3(256), 0, stream, a);
     else if (S == 4) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 4, OutT>), grid, dim3(256), 0, stream, a);
@@ -269,6 +269,8 @@ hipError_t launch_skinny_wide(const Call& c, hipStream_t stream) {
     r.M = (int)c.M; r.N = (int)c.N; r.ldc = (int)c.ldc;
     r.strideC = c.sC;
     r.tiles_n = a.tiles_n; r.tiles_m = (int)tm;
+    const long long ob = (long long)sizeof(OutT);
+    r.c_vec = aligned16(c.C) && (c.ldc * ob) % 16 == 0 && (c.sC * ob) % 16 == 0;
     for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
         long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;

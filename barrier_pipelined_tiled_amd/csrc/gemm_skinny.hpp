@@ -348,24 +348,49 @@ struct SkinnySumArgs {
     long long strideC;
     int tiles_n, tiles_m;
     long long blocks;       // blocks of this launch
+    int c_vec;              // C rows and batch entries start 16-byte aligned
 };
 
+template <typename OutT>
+__device__ inline void store8(OutT* dst, float4_t lo, float4_t hi) {
+    if constexpr (sizeof(OutT) == 4) {
+        *(float4_t*)dst = lo;
+        *(float4_t*)(dst + 4) = hi;
+    } else {
+        typedef OutT out8_t __attribute__((ext_vector_type(8)));
+        out8_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[q] = cvt_out<OutT>(lo[q]);
+            v[q + 4] = cvt_out<OutT>(hi[q]);
+        }
+        *(out8_t*)dst = v;
+    }
+}
+
 // C block = sum over splits of the partial blocks, in split order.  One
-// thread per 4 consecutive outputs of a block row.
+// thread per 8 consecutive outputs of a block row: 2S 16-byte loads issued
+// together, one 16-byte (or two) store when C's rows allow it.
 template <int BN, int S, typename OutT>
 __global__ __launch_bounds__(256) void skinny_sum_kernel(SkinnySumArgs args) {
     constexpr int BLOCK = 64 * BN;
     const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long blk = gid / (BLOCK / 4);
+    const long long blk = gid / (BLOCK / 8);
     if (blk >= args.blocks) return;
-    const int e = (int)(gid - blk * (BLOCK / 4)) * 4;
+    const int e = (int)(gid - blk * (BLOCK / 8)) * 8;
     const float* p = args.partial + blk * S * BLOCK + e;
-    float4_t v[S];
+    float4_t v[S][2];
 #pragma unroll
-    for (int q = 0; q < S; ++q) v[q] = *(const float4_t*)(p + q * BLOCK);
-    float4_t s = v[0];
+    for (int q = 0; q < S; ++q) {
+        v[q][0] = *(const float4_t*)(p + q * BLOCK);
+        v[q][1] = *(const float4_t*)(p + q * BLOCK + 4);
+    }
+    float4_t lo = v[0][0], hi = v[0][1];
 #pragma unroll
-    for (int q = 1; q < S; ++q) s += v[q];
+    for (int q = 1; q < S; ++q) {
+        lo += v[q][0];
+        hi += v[q][1];
+    }
     const int tn = (int)(blk % args.tiles_n);
     const long long rest = blk / args.tiles_n;
     const int tm = (int)(rest % args.tiles_m);
@@ -373,9 +398,15 @@ __global__ __launch_bounds__(256) void skinny_sum_kernel(SkinnySumArgs args) {
     const int row = tm * 64 + e / BN, col = tn * BN + e % BN;
     if (row >= args.M) return;
     OutT* dst = static_cast<OutT*>(args.C) + batch * args.strideC + (long long)row * args.ldc + col;
+    if (args.c_vec && col + 8 <= args.N) {
+        store8<OutT>(dst, lo, hi);
+        return;
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (col + q < args.N) dst[q] = cvt_out<OutT>(s[q]);
+    for (int q = 0; q < 4; ++q) {
+        if (col + q < args.N) dst[q] = cvt_out<OutT>(lo[q]);
+        if (col + 4 + q < args.N) dst[4 + q] = cvt_out<OutT>(hi[q]);
+    }
 }
 
 }  // namespace bpt

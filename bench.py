@@ -39,28 +39,33 @@ def log(msg):
 
 
 def kernel_source_sha() -> str:
-    """Hash of the sources the pipelined kernels are built from."""
+    """Hash of every kernel and launcher source (any change voids the stored
+    counter readings)."""
     import hashlib
     h = hashlib.sha256()
-    for rel in ("gemm_pipelined.hpp", "device_common.hpp", "api.hip"):
-        with open(os.path.join(ROOT, "barrier_pipelined_tiled_amd", "csrc", rel), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "barrier_pipelined_tiled_amd", "csrc")
+    for rel in sorted(os.listdir(csrc)):
+        if rel.endswith((".hpp", ".hip")):
+            with open(os.path.join(csrc, rel), "rb") as f:
+                h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
-    scaled by the copy-kernel calibration; None when no run exists for this
-    kernel or the kernel sources changed since it was taken."""
+    """HBM bytes per step from the committed counter runs (profiles/traffic.json):
+    FETCH_SIZE and WRITE_SIZE per dispatch, summed over the kernels of one
+    step and scaled by the copy-kernel calibration; None when no run exists
+    for this variant or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     e = t.get("entries", {}).get(workload)
-    if not e or e.get("kernel") != kernel or e.get("source_sha") != kernel_source_sha():
+    if not e or e.get("variant") != kernel or e.get("source_sha") != kernel_source_sha():
         return None
-    return int(round((e["fetch_kib"] * t["fetch_scale"] + e["write_kib"] * t["write_scale"]) * 1024))
+    kib = sum(k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"] for k in e["kernels"])
+    return int(round(kib * 1024))
 
 
 def cpu_baseline(w, A, B, budget_s: float = 12.0):
