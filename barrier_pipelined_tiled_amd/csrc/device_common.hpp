@@ -68,6 +68,16 @@ __device__ inline void publish() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Lanes of one wave hand data to each other through LDS (write by one lane,
+// read by another).  The hardware runs a wave's LDS instructions in order,
+// but the compiler sees unsynchronised accesses of different lanes and may
+// reorder them; this fence orders them at wave scope (no instruction is
+// emitted for it).
+__device__ inline void wave_lds_handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <typename T>
 struct Mfma;
 

@@ -408,6 +408,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
                     *(BPT_LDS out4_t*)(stage_w + r * G::EPI_PITCH + c * OB) = v;
                 }
         }
+        wave_lds_handoff();                        // rows written by other lanes are read below
 #pragma unroll
         for (int it = 0; it < G::EPI_ROWS / ROWS_PER_IT; ++it) {
             const int r = it * ROWS_PER_IT + lane / CH_PER_ROW;
@@ -416,16 +417,19 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
             const int grow = row0 + pass * G::EPI_ROWS + r;
             const int gcol = col0 + ch * (16 / OB);
             OutT* dst = Cb + (long long)grow * ldc + gcol;
-            if (vec) {
-                *(int4_t*)dst = v;
-            } else if (grow < M) {
-                OutT vals[16 / OB];
-                __builtin_memcpy(vals, &v, 16);
-#pragma unroll
-                for (int e = 0; e < 16 / OB; ++e)
-                    if (gcol + e < N) dst[e] = vals[e];
+            // N % 8 == 0: a 16-byte chunk is wholly inside C or wholly outside
+            if (vec || (grow < M && gcol < N)) {
+                if (args.c_vec) {
+                    *(int4_t*)dst = v;
+                } else {
+                    OutT vals[16 / OB];
+                    __builtin_memcpy(vals, &v, 16);
+#pragma unroll 1
+                    for (int e = 0; e < 16 / OB; ++e) dst[e] = vals[e];
+                }
             }
         }
+        wave_lds_handoff();                        // the next pass overwrites what was just read
     }
 }
 
