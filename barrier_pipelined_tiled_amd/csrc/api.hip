@@ -60,6 +60,9 @@ const char* const kVariantNames[] = {
 // K-tile and stage count of each pipelined variant (0 for the others)
 constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0};
 constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0};
+// which of them take K % BK != 0 (see pipelined_ok); filled below from the
+// kernels' own layout
+bool variant_tail(int v);
 
 
 struct Call {
@@ -75,11 +78,19 @@ constexpr long long kI31 = (1LL << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Does the pipelined kernel with this tile give the partial last K-tile a
+// stage of its own (ring + one stage fit in LDS)?
+template <int BM, int BN, int BK, int STAGES>
+constexpr bool kTail = bpt::PipelinedGemm<_Float16, BM, BN, BK, STAGES, 2, 2, _Float16>::TAIL;
+
 // Can a pipelined variant with K-tile BK and STAGES ring stages take this
-// call?  The prologue fills every stage, so K must span at least STAGES tiles.
-// Column chunks of B are 8 wide and must not straddle N: N % 8 == 0.
-bool pipelined_ok(const Call& c, int BK, int STAGES) {
-    if (c.K <= 0 || c.K % BK != 0 || c.K / BK < STAGES) return false;
+// call?  The prologue fills every stage, so K must span at least STAGES full
+// tiles; a partial last tile needs the tail stage (`tail`) and K % 8 == 0
+// (A chunks of 8 k values are wholly inside K or wholly past it).  Column
+// chunks of B are 8 wide and must not straddle N: N % 8 == 0.
+bool pipelined_ok(const Call& c, int BK, int STAGES, bool tail) {
+    if (c.K <= 0 || c.K / BK < STAGES) return false;
+    if (c.K % BK != 0 && !(tail && c.K % 8 == 0)) return false;
     if (c.N % 8 != 0) return false;
     if (!aligned16(c.A) || !aligned16(c.B)) return false;
     if (c.lda % 8 != 0 || c.ldb % 8 != 0) return false;
@@ -177,6 +188,17 @@ float* stream_workspace(long long bytes, hipStream_t stream) {
     return static_cast<float*>(p);
 }
 
+bool variant_tail(int v) {
+    switch (v) {
+        case V_PIPE_256_K64_S2: return kTail<256, 256, 64, 2>;
+        case V_PIPE_128_K64_S2: return kTail<128, 128, 64, 2>;
+        case V_PIPE_256_K32_S4: return kTail<256, 256, 32, 4>;
+        case V_PIPE_256_K32_S5: return kTail<256, 256, 32, 5>;
+        case V_PIPE_128_K32_S4: return kTail<128, 128, 32, 4>;
+        default: return false;
+    }
+}
+
 int choose(const Call& c) {
     long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     // few rows of A: stream B once with a skinny kernel when that yields at
@@ -188,10 +210,10 @@ int choose(const Call& c) {
         if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
     }
     const bool big = tiles256 >= 128;
-    if (big && pipelined_ok(c, 32, 4)) return V_PIPE_256_K32_S4;
-    if (pipelined_ok(c, 32, 4)) return V_PIPE_128_K32_S4;
-    if (big && pipelined_ok(c, 64, 2)) return V_PIPE_256_K64_S2;
-    if (pipelined_ok(c, 64, 2)) return V_PIPE_128_K64_S2;
+    if (big && pipelined_ok(c, 32, 4, variant_tail(V_PIPE_256_K32_S4))) return V_PIPE_256_K32_S4;
+    if (pipelined_ok(c, 32, 4, variant_tail(V_PIPE_128_K32_S4))) return V_PIPE_128_K32_S4;
+    if (big && pipelined_ok(c, 64, 2, variant_tail(V_PIPE_256_K64_S2))) return V_PIPE_256_K64_S2;
+    if (pipelined_ok(c, 64, 2, variant_tail(V_PIPE_128_K64_S2))) return V_PIPE_128_K64_S2;
     return V_GENERIC;
 }
 
@@ -361,7 +383,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_SKINNY: return skinny_ok(c);
         case V_SKINNY_WIDE: return wide_splits(c) > 0;
         default:
-            if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v]);
+            if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;
     }
 }

@@ -151,7 +151,11 @@ struct PipelinedGemm {
     static constexpr int EPI_ROWS = TM / EPI_PASSES;
     static constexpr int EPI_PITCH = TN * (int)sizeof(OutT) + 16;   // bytes, padded
     static constexpr int EPI_BYTES = 4 * EPI_ROWS * EPI_PITCH;
-    static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    // K % BK != 0: the partial last K-tile gets a stage of its own behind the
+    // ring, when that fits
+    static constexpr bool TAIL = RING_BYTES + STAGE_BYTES <= 160 * 1024;
+    static constexpr int MAIN_BYTES = RING_BYTES + (TAIL ? STAGE_BYTES : 0);
+    static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 
     typedef typename Mfma<T>::frag_t frag_t;
@@ -315,7 +319,36 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     // window, slices 1 .. KS-1 in k-steps 0 .. KS-2 of tile j+1, so the load
     // path never sees a burst.  All of them are issued before publish(j+2),
     // which therefore still waits for exactly STAGES-2 younger groups.
-    const int nk = K / BK;                 // host guarantees K % BK == 0 and nk >= STAGES
+    const int nk = K / BK;                 // full K-tiles; host guarantees nk >= STAGES
+
+    // ---- K tail: K = nk*BK + ktail, 0 < ktail < BK, ktail % 8 == 0 (host) -----
+    // The partial K-tile is copied first, into stage STAGES, with every copy
+    // of k >= K pointed past num_records so it reads zeros (A chunks of 8 k
+    // values and B rows are wholly valid or wholly not).  Being the oldest
+    // copies in flight, they have landed once the first publish below has
+    // waited for tile 0, and its barrier shows them to every wave.  The tail
+    // K-tile is consumed after the last full one.
+    const int ktail = K - nk * BK;
+    if constexpr (G::TAIL) {
+        if (ktail != 0) {
+            const uint32_t tbase = lds0 + STAGES * G::STAGE_BYTES;
+            const uint32_t tkA = (uint32_t)(nk * BK * 2);
+            const uint32_t tkB = (uint32_t)nk * BK * ldb * 2;
+            constexpr uint32_t kPast = 0x80000000u;        // beyond any extent the host allows
+#pragma unroll
+            for (int i = 0; i < G::A_INST_W; ++i) {
+                int row = (wave * G::A_INST_W + i) * G::A_ROWS_PER_INST + lane / G::A_CHUNKS;
+                int chunk = (lane % G::A_CHUNKS) ^ swz_a<BK>(row);
+                dma16(rsA, tbase + (wave * G::A_INST_W + i) * 1024, chunk * 8 < ktail ? voffA[i] : kPast, tkA);
+            }
+#pragma unroll
+            for (int i = 0; i < G::B_INST_W; ++i) {
+                int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
+                dma16(rsB, tbase + G::A_STAGE * 2 + (wave * G::B_INST_W + i) * 1024,
+                      row < ktail ? voffB[i] : kPast, tkB);
+            }
+        }
+    }
     uint32_t kA = 0, kB = 0;               // byte offsets of the next tile to copy
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) {
@@ -373,6 +406,16 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
                              : tile.template operator()<false, false, 0, true>()),
          ...);
     }(std::make_integer_sequence<int, STAGES - 1>{});
+
+    // the tail K-tile, from its own stage (landed and published long ago)
+    if constexpr (G::TAIL) {
+        if (ktail != 0) {
+#pragma unroll
+            for (int p = 0; p < G::NREAD; ++p) read_piece(STAGES, 0, p, 0);
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) kstep(ks & 1, ks + 1 < G::KS, STAGES, ks + 1, false, 0, 0, 0, 0);
+        }
+    }
 
     // ---- a8: epilogue ---------------------------------------------------------
     // Result layout (B fragment as first MFMA operand): lane l, register r of

@@ -166,7 +166,10 @@ def main():
 
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
-    memory_bound = w.name.startswith("f16_skinny")
+    # the bound: HBM when the workload's flops per compulsory byte fall below
+    # the machine balance (2516.6 TFLOP/s / 8 TB/s = 315 flop/B); the batched
+    # short-K shape (228, its fp16 C writes) and the skinny shape (63) are
+    memory_bound = flops / w.compulsory_bytes < PEAK_MFMA_F16_TFLOPS / PEAK_HBM_GBS * 1e3
     if memory_bound:
         achieved = w.compulsory_bytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -127,8 +127,12 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 256, 256, 96, 96, 256) == v["generic_64x64x16"]
     # K = 128: four 32-wide tiles fill the four-stage ring
     assert pkg.select_variant("f16", 1, 4096, 4096, 128, 128, 4096) == big
-    # K not a multiple of 64, odd leading dimension, unaligned base: generic
-    assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["generic_64x64x16"]
+    # K = 200 = 6 x 32 + 8: six full K-tiles and a partial one in its own stage
+    assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["pipelined_128x128x32_s4"]
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4104, 4104, 4096) == big
+    # K % 8 != 0 (a chunk of A would straddle K), odd leading dimension,
+    # unaligned base: generic
+    assert pkg.select_variant("f16", 1, 256, 256, 196, 196, 256) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == v["generic_64x64x16"]
     assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == v["generic_64x64x16"]
     # K = 64 is one 64-wide tile (two stages need two) and two 32-wide tiles

@@ -74,6 +74,12 @@ VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64
 SHAPES_PIPE = [(256, 256, 256), (512, 384, 320), (300, 200, 192), (1, 8, 256), (33, 520, 192),
                (129, 136, 256), (640, 768, 512), (256, 512, 1024)]
 SHAPES_GENERIC_ONLY = [(100, 70, 50), (5, 3, 1), (257, 65, 129), (129, 129, 64), (64, 64, 64), (96, 201, 256)]
+# K % BK != 0 with K % 8 == 0: the variants whose ring leaves room for a tail
+# stage copy the partial last K-tile first and consume it last.  K = 136 has
+# exactly as many full 32-wide tiles as the 4-stage ring (and two 64-wide
+# ones); 200, 248 and 1032 leave tails of 8, 24 and 8 (64-wide: 8, 56, 8)
+TAIL_VARIANTS = ["pipelined_128x128x64_s2", "pipelined_256x256x32_s4", "pipelined_128x128x32_s4"]
+SHAPES_KTAIL = [(256, 256, 136), (300, 264, 200), (129, 520, 248), (384, 512, 1032), (1, 8, 136)]
 
 
 # the skinny variant splits K over 4 waves in 64-deep chunks, 4 per wave at
@@ -94,7 +100,10 @@ def _shapes(vname):
         return SHAPES_SKINNY + SHAPES_WIDE_ONLY
     if vname.startswith("skinny"):
         return SHAPES_SKINNY
-    return SHAPES_PIPE + (SHAPES_GENERIC_ONLY if vname.startswith("generic") else [])
+    extra = SHAPES_GENERIC_ONLY if vname.startswith("generic") else []
+    if vname in TAIL_VARIANTS or vname.startswith("generic"):
+        extra = extra + SHAPES_KTAIL
+    return SHAPES_PIPE + extra
 
 
 @pytest.mark.parametrize("vname", VARIANTS)
@@ -140,7 +149,7 @@ def test_identity_and_permutation_exact():
 
 
 PADDED_CASES = [(v, 70, 200, 2048) if v.startswith("skinny") else (v, 300, 200, 192) for v in VARIANTS] + \
-    [("generic_64x64x16", 300, 201, 200)]
+    [("generic_64x64x16", 300, 201, 200)] + [(v, 300, 200, 200) for v in TAIL_VARIANTS]
 
 
 @pytest.mark.parametrize("vname,M,N,K", PADDED_CASES)
