@@ -164,6 +164,19 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (events)")
 
+    # per-call spread, after and outside the timed block: each call between
+    # its own pair of events on the launch stream
+    n_calls = min(50, max(10, args.steps // 4))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
+    spread = {"calls": n_calls, "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
+
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
     # the bound: HBM when the workload's flops per compulsory byte fall below
@@ -206,6 +219,7 @@ def main():
                    "pct_of_dense_peak": 100.0 * value / PEAK_MFMA_F16_TFLOPS},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "per_call": spread,
     }
     print(json.dumps(out), flush=True)
 

@@ -289,18 +289,21 @@ def _full_size(w, A, B):
 FULL = ["f16_4096", "bf16_4096x4096x16384", "f16_batched_64x4096x4096x256", "f16_skinny_64x8192x8192"]
 
 
+@pytest.mark.parametrize("which", ["first", "last"])
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, which):
+    """The benchmark's first and last rotating input set at full size."""
     w = inputs.WORKLOADS[name]
-    say(f"[full] {name}")
-    A, B = w.make_a(0), w.make_b(0)
+    j = 0 if which == "first" else w.rotating - 1
+    say(f"[full] {name} set {j}")
+    A, B = w.make_a(j), w.make_b(j)
     assert pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.N, w.out_fp32) != \
         pkg.variants()["generic_64x64x16"]
     finite, vals, (b, r, c) = _full_size(w, A, B)
     assert finite, "non-finite values in the output"
     ref = oracle.gemm_at(inputs.bits(A), inputs.bits(B), b, r, c, w.dtype)
     m = oracle.compare(vals.float().cpu().numpy(), ref, w.K)
-    say(f"[full] {name} rel_rms={m['rel_rms']:.3e} max_abs={m['max_abs']:.3e}")
+    say(f"[full] {name} set {j} rel_rms={m['rel_rms']:.3e} max_abs={m['max_abs']:.3e}")
     assert m["ok"], m
 
 
