@@ -20,6 +20,7 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    "-Wl,--no-undefined",           # a missing definition fails the build, not the load
 ]
 
 

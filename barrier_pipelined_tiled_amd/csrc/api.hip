@@ -155,12 +155,23 @@ int wide_splits(const Call& c) {
     return best;
 }
 
-// One device workspace per (device, stream), grown on demand and kept until
-// the process ends; nullptr when it cannot be had (allocation failure, or the
-// stream is being captured, where allocating is not allowed).
+// One device workspace per (device, stream), grown on demand.  A grown-out
+// buffer is kept, not freed, until the process ends: a call on another host
+// thread may still hold its address, and nothing here can tell when that
+// call's kernels are done with it (the waste stays below the final size,
+// since each buffer is at least twice the one before).  nullptr when no
+// workspace may be used: the allocation fails, or the stream is being
+// captured into a graph -- a graph must not hold the address of a buffer
+// that a later call could outgrow, so captured calls run unsplit.
 float* stream_workspace(long long bytes, hipStream_t stream) {
     static std::mutex mu;
     static std::map<std::pair<int, hipStream_t>, std::pair<void*, long long>> spaces;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (cap != hipStreamCaptureStatusNone) return nullptr;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
@@ -169,20 +180,12 @@ float* stream_workspace(long long bytes, hipStream_t stream) {
     std::lock_guard<std::mutex> lock(mu);
     auto& w = spaces[{dev, stream}];
     if (w.second >= bytes) return static_cast<float*>(w.first);
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) (void)hipGetLastError();
-    if (cap != hipStreamCaptureStatusNone) return nullptr;
     long long want = bytes > 2 * w.second ? bytes : 2 * w.second;
     if (want > kWorkspaceMax) want = bytes;
     void* p = nullptr;
     if (hipMalloc(&p, (size_t)want) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
-    }
-    if (w.first != nullptr) {
-        // the old workspace is only ever used on this stream
-        (void)hipStreamSynchronize(stream);
-        (void)hipFree(w.first);
     }
     w = {p, want};
     return static_cast<float*>(p);

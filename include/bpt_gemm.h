@@ -25,13 +25,13 @@
  * the workspace of the split-K path for few rows of A (variant
  * skinny_64x128_w4_k32_s4_splitk when it splits K over workgroups): one
  * device buffer per (device, stream), allocated with hipMalloc by the first
- * call on that stream that needs it, replaced by a larger one when a later
- * call needs more (that call synchronises the stream before freeing the old
- * one), and kept until the process exits -- at most 256 MiB each.  Calls on
- * one stream use it in stream order; calls on different streams never share
- * one.  A call that cannot get it (the allocation fails, or the stream is
- * being captured into a graph) runs the same kernel without splitting K,
- * which needs no workspace.
+ * call on that stream that needs it and replaced by a larger one (at least
+ * twice the size) when a later call needs more.  No buffer is freed before
+ * the process exits; each is at most 256 MiB.  Calls on one stream use it in
+ * stream order; calls on different streams never share one.  A call made
+ * while its stream is being captured into a graph, or one whose allocation
+ * fails, runs the same kernel without splitting K, which needs no
+ * workspace -- so a captured graph never refers to a library buffer.
  *
  * Execution: the call validates its arguments on the host, enqueues the
  * kernel(s) on `stream` (NULL = the default stream) and returns without

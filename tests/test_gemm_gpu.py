@@ -224,6 +224,42 @@ def test_repeat_runs_bitwise_identical():
         assert torch.equal(o, outs[0])
 
 
+def test_graph_capture_of_a_split_k_call():
+    """A call captured into a graph must not use the per-stream workspace (a
+    graph would keep its address): captured, the wide skinny path runs
+    unsplit.  Exact-integer inputs make the split (eager) and unsplit
+    (captured) sums bit-identical, so every replay -- with eager calls and
+    synchronisations between replays -- must equal the oracle exactly."""
+    M, N, K = 64, 2048, 4096                      # wide skinny kernel, 8 splits when eager
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
+    A = inputs.small_integers((M, K), 7501)
+    B = inputs.small_integers((K, N), 7502)
+    ref = torch.from_numpy(oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"))
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    pkg.gemm_f16(Ad, Bd, C, out_fp32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                 # warm-up on a side stream, as torch advises
+        pkg.gemm_f16(Ad, Bd, C, out_fp32=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkg.gemm_f16(Ad, Bd, C, out_fp32=True)
+    for rep in range(3):
+        C.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.cpu(), ref), rep
+        eager = pkg.gemm_f16(Ad, Bd, out_fp32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.cpu(), ref), rep
+
+
 def test_split_k_workspace_streams_and_growth():
     """The split-K path keeps one workspace per stream: calls on two streams
     in flight together, and a call that needs a larger workspace after a
