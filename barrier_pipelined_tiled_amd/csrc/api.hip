@@ -16,6 +16,7 @@
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
+#include "repack.hpp"
 
 namespace {
 
@@ -42,7 +43,8 @@ enum Variant {
     V_PIPE_128_K32_S4 = 6,  // 128x128 tile, BK 32, 4 stages
     V_SKINNY = 7,           // 64x32 block over all of K, 4 waves split K, per-wave LDS rings
     V_SKINNY_WIDE = 8,      // 64x128 block, K also split over workgroups, + split-sum kernel
-    V_COUNT = 8
+    V_REPACK = 9,           // zero-padded aligned copies of A and B, then a pipelined kernel
+    V_COUNT = 9
 };
 
 const char* const kVariantNames[] = {
@@ -55,11 +57,12 @@ const char* const kVariantNames[] = {
     "pipelined_128x128x32_s4",
     "skinny_64x32_w4_k64_s4",
     "skinny_64x128_w4_k32_s4_splitk",
+    "repack_pipelined",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -72,6 +75,7 @@ struct Call {
     const void* B;
     void* C;
     int out_fp32;
+    long long nb = 0;       // columns of B when it is a padded copy (0: N)
 };
 
 constexpr long long kI31 = (1LL << 31) - 1;
@@ -87,18 +91,20 @@ constexpr bool kTail = bpt::PipelinedGemm<_Float16, BM, BN, BK, STAGES, 2, 2, _F
 // call?  The prologue fills every stage, so K must span at least STAGES full
 // tiles; a partial last tile needs the tail stage (`tail`) and K % 8 == 0
 // (A chunks of 8 k values are wholly inside K or wholly past it).  Column
-// chunks of B are 8 wide and must not straddle N: N % 8 == 0.
+// chunks of B are 8 wide and must not straddle B's width: N % 8 == 0, or
+// for a padded copy of B its width (c.nb) % 8 == 0.
 bool pipelined_ok(const Call& c, int BK, int STAGES, bool tail) {
+    const long long nb = c.nb > 0 ? c.nb : c.N;
     if (c.K <= 0 || c.K / BK < STAGES) return false;
     if (c.K % BK != 0 && !(tail && c.K % 8 == 0)) return false;
-    if (c.N % 8 != 0) return false;
+    if (nb % 8 != 0 || nb < c.N || nb > c.ldb) return false;
     if (!aligned16(c.A) || !aligned16(c.B)) return false;
     if (c.lda % 8 != 0 || c.ldb % 8 != 0) return false;
     if (c.sA % 8 != 0 || c.sB % 8 != 0) return false;
     // buffer offsets are 32-bit: each operand's extent (plus one tile of
     // rows past M) must stay below 2^31 bytes
     long long extA = ((c.M + 256) * c.lda + c.K) * 2;
-    long long extB = (c.K * c.ldb + c.N + 256) * 2;
+    long long extB = (c.K * c.ldb + nb + 256) * 2;
     if (extA > kI31 || extB > kI31) return false;
     return true;
 }
@@ -191,6 +197,79 @@ float* stream_workspace(long long bytes, hipStream_t stream) {
     return static_cast<float*>(p);
 }
 
+// the pipelined variant for a call one of them accepts in place (or for its
+// repacked form); V_GENERIC when none does
+int choose_pipelined(const Call& c) {
+    const long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
+    const bool big = tiles256 >= 128;
+    if (big && pipelined_ok(c, 32, 4, variant_tail(V_PIPE_256_K32_S4))) return V_PIPE_256_K32_S4;
+    if (pipelined_ok(c, 32, 4, variant_tail(V_PIPE_128_K32_S4))) return V_PIPE_128_K32_S4;
+    if (big && pipelined_ok(c, 64, 2, variant_tail(V_PIPE_256_K64_S2))) return V_PIPE_256_K64_S2;
+    if (pipelined_ok(c, 64, 2, variant_tail(V_PIPE_128_K64_S2))) return V_PIPE_128_K64_S2;
+    return V_GENERIC;
+}
+
+// ---- repack route ------------------------------------------------------------
+// A call no fast path reads in place (odd N or K, leading dimensions or bases
+// not 16-byte aligned) is copied into zero-padded, aligned A' (M x K') and
+// B' (K' x N'), K' and N' rounded up to 8, and the pipelined kernel runs on
+// the copies, storing C at its true N.  Worth it when the product is large
+// enough for the copies (each operand read and written once) to be small
+// against the guarded kernel's time; limited by the workspace.
+constexpr long long kRepackMax = 1LL << 30;        // workspace bytes per (device, stream)
+
+long long round8(long long x) { return (x + 7) / 8 * 8; }
+
+// Which operands need the copy.  With K % 8 == 0 an operand whose base,
+// leading dimension and batch stride are 16-byte granular (and, for B,
+// whose N is a multiple of 8) is read in place; K % 8 != 0 pads both.
+bool repack_a(const Call& c) {
+    return c.K % 8 != 0 || !aligned16(c.A) || c.lda % 8 != 0 || c.sA % 8 != 0;
+}
+bool repack_b(const Call& c) {
+    return c.K % 8 != 0 || !aligned16(c.B) || c.ldb % 8 != 0 || c.sB % 8 != 0 || c.N % 8 != 0;
+}
+
+long long repack_a_bytes(const Call& c) {
+    return repack_a(c) ? (c.batch * c.M * round8(c.K) * 2 + 255) / 256 * 256 : 0;
+}
+
+long long repack_bytes(const Call& c) {
+    return repack_a_bytes(c) + (repack_b(c) ? c.batch * round8(c.K) * round8(c.N) * 2 : 0);
+}
+
+Call repacked_call(const Call& c, void* ws) {
+    const long long Kp = round8(c.K), Np = round8(c.N);
+    Call r = c;
+    r.K = Kp;
+    if (repack_a(c)) {
+        r.lda = Kp;
+        r.sA = c.batch > 1 ? c.M * Kp : 0;
+        r.A = ws;
+    }
+    if (repack_b(c)) {
+        r.ldb = Np;
+        r.sB = c.batch > 1 ? Kp * Np : 0;
+        r.nb = Np;
+        r.B = static_cast<char*>(ws) + repack_a_bytes(c);
+    }
+    return r;
+}
+
+// would the repacked call run on a pipelined variant (within the workspace
+// limit)?
+bool repack_feasible(const Call& c) {
+    if (c.K <= 0 || c.M <= 0 || c.N <= 0 || c.batch <= 0) return false;
+    if (repack_bytes(c) > kRepackMax) return false;
+    alignas(256) static char probe[256];           // stands in for the 256-byte aligned workspace
+    return choose_pipelined(repacked_call(c, probe)) != V_GENERIC;
+}
+
+// ... and is the product large enough (16 M multiply-adds) to pay for it?
+bool repack_ok(const Call& c) {
+    return (double)c.batch * c.M * c.N * c.K >= (double)(1 << 24) && repack_feasible(c);
+}
+
 bool variant_tail(int v) {
     switch (v) {
         case V_PIPE_256_K64_S2: return kTail<256, 256, 64, 2>;
@@ -203,7 +282,6 @@ bool variant_tail(int v) {
 }
 
 int choose(const Call& c) {
-    long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     // few rows of A: stream B once with a skinny kernel when that yields at
     // least half a workgroup per CU; the wide one reads B in 256-byte row
     // pieces, which stream faster than the narrow one's 64-byte pieces
@@ -212,11 +290,9 @@ int choose(const Call& c) {
         if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_WIDE;
         if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
     }
-    const bool big = tiles256 >= 128;
-    if (big && pipelined_ok(c, 32, 4, variant_tail(V_PIPE_256_K32_S4))) return V_PIPE_256_K32_S4;
-    if (pipelined_ok(c, 32, 4, variant_tail(V_PIPE_128_K32_S4))) return V_PIPE_128_K32_S4;
-    if (big && pipelined_ok(c, 64, 2, variant_tail(V_PIPE_256_K64_S2))) return V_PIPE_256_K64_S2;
-    if (pipelined_ok(c, 64, 2, variant_tail(V_PIPE_128_K64_S2))) return V_PIPE_128_K64_S2;
+    const int v = choose_pipelined(c);
+    if (v != V_GENERIC) return v;
+    if (repack_ok(c)) return V_REPACK;
     return V_GENERIC;
 }
 
@@ -231,6 +307,7 @@ hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
     a.group_m = 4;
     const long long ob = (long long)sizeof(OutT);
     a.c_vec = aligned16(c.C) && (c.ldc * ob) % 16 == 0 && (c.sC * ob) % 16 == 0;
+    a.nb = (int)(c.nb > 0 ? c.nb : c.N);
     const long long tiles = (long long)a.tiles_m * a.tiles_n;
     for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
         long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
@@ -346,6 +423,41 @@ hipError_t launch_zero(const Call& c, hipStream_t stream) {
 }
 
 template <typename T, typename OutT>
+hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream);
+
+void launch_repack_copy(const void* src, long long ld, long long stride, void* dst, long long ldd, long long strided,
+                        long long batch, long long rows, long long cols, long long rows_p, long long cols_p,
+                        hipStream_t stream) {
+    bpt::RepackArgs a;
+    a.src = src; a.dst = dst;
+    a.ld = ld; a.stride = stride; a.ldd = ldd; a.strided = strided;
+    a.rows = (int)rows; a.cols = (int)cols; a.rows_p = (int)rows_p; a.cols_p = (int)cols_p;
+    a.total8 = batch * rows_p * cols_p / 8;
+    long long blocks = (a.total8 + 255) / 256;
+    if (blocks > 16384) blocks = 16384;            // grid-stride loop covers the rest
+    if (blocks > 0)
+        hipLaunchKernelGGL(bpt::repack_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+}
+
+// Copy A and B into the stream's workspace, zero-padded and aligned, then run
+// the pipelined kernel on the copies.  Without a workspace (graph capture,
+// allocation failure) the guarded kernel takes the call as it is.
+template <typename T, typename OutT>
+hipError_t launch_repack(const Call& c, hipStream_t stream) {
+    if (repack_bytes(c) == 0) return dispatch_typed<T, OutT>(c, choose_pipelined(c), stream);   // nothing to copy
+    void* ws = stream_workspace(repack_bytes(c), stream);
+    if (ws == nullptr) return launch_generic<T, OutT>(c, stream);
+    const Call r = repacked_call(c, ws);
+    if (repack_a(c))
+        launch_repack_copy(c.A, c.lda, c.sA, const_cast<void*>(r.A), r.lda, c.M * r.lda, c.batch, c.M, c.K, c.M,
+                           r.K, stream);
+    if (repack_b(c))
+        launch_repack_copy(c.B, c.ldb, c.sB, const_cast<void*>(r.B), r.ldb, r.K * r.ldb, c.batch, c.K, c.N, r.K,
+                           r.nb, stream);
+    return dispatch_typed<T, OutT>(r, choose_pipelined(r), stream);
+}
+
+template <typename T, typename OutT>
 hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
     if (c.K == 0) return launch_zero<OutT>(c, stream);
     switch (v) {
@@ -356,6 +468,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PIPE_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4>(c, stream);
         case V_SKINNY: return launch_skinny<T, OutT>(c, stream);
         case V_SKINNY_WIDE: return launch_skinny_wide<T, OutT>(c, stream);
+        case V_REPACK: return launch_repack<T, OutT>(c, stream);
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -385,6 +498,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_GENERIC: return true;
         case V_SKINNY: return skinny_ok(c);
         case V_SKINNY_WIDE: return wide_splits(c) > 0;
+        case V_REPACK: return repack_feasible(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

@@ -53,6 +53,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int group_m;                           // tile rows per group in the walk order
     int c_vec;                             // C rows 16-byte aligned: vector stores allowed
+    int nb;                                // columns of B (N, or N rounded up to 8 when B
+                                           // is a zero-padded copy); N bounds the C stores
 };
 
 // ---------------------------------------------------------------------------
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     // ---- a3: descriptors once, per-lane offsets once -------------------------
     // Extent of each operand in bytes: anything at or beyond reads as zero.
     const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
-    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + N) * 2));
+    const int NB_ = args.nb;               // host: NB_ % 8 == 0, N <= NB_ <= ldb
+    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + NB_) * 2));
 
     uint32_t voffA[G::A_INST_W];
 #pragma unroll
@@ -199,16 +202,16 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         int chunk = (lane % G::A_CHUNKS) ^ swz_a<BK>(row);
         voffA[i] = (uint32_t)(((m0 + row) * lda + chunk * 8) * 2);
     }
-    // A lane whose 8 columns of B start at or past N fetches the last
-    // in-bounds chunk instead (host: N % 8 == 0), so no copy ever reads past
-    // the end of B; those columns of C are never stored.
+    // A lane whose 8 columns of B start at or past B's width fetches the last
+    // in-bounds chunk instead (host: the width is a multiple of 8), so no copy
+    // ever reads past the end of B; those columns of C are never stored.
     uint32_t voffB[G::B_INST_W];
 #pragma unroll
     for (int i = 0; i < G::B_INST_W; ++i) {
         int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
         int chunk = (lane % G::B_CHUNKS) ^ swz_b(row);
         int col = n0 + chunk * 8;
-        if (col >= N) col = N - 8;
+        if (col >= NB_) col = NB_ - 8;
         voffB[i] = (uint32_t)((row * ldb + col) * 2);
     }
     const uint32_t a_step = BK * 2;                        // bytes per K-tile
@@ -460,15 +463,17 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
             const int grow = row0 + pass * G::EPI_ROWS + r;
             const int gcol = col0 + ch * (16 / OB);
             OutT* dst = Cb + (long long)grow * ldc + gcol;
-            // N % 8 == 0: a 16-byte chunk is wholly inside C or wholly outside
+            // a 16-byte chunk is wholly inside C or outside when N % 8 == 0;
+            // only repacked calls (N % 8 != 0) have chunks that straddle N
             if (vec || (grow < M && gcol < N)) {
-                if (args.c_vec) {
+                if (args.c_vec && gcol + 16 / OB <= N) {
                     *(int4_t*)dst = v;
                 } else {
                     OutT vals[16 / OB];
                     __builtin_memcpy(vals, &v, 16);
 #pragma unroll 1
-                    for (int e = 0; e < 16 / OB; ++e) dst[e] = vals[e];
+                    for (int e = 0; e < 16 / OB; ++e)
+                        if (gcol + e < N) dst[e] = vals[e];
                 }
             }
         }

@@ -22,22 +22,31 @@
  *
  * Ownership: A, B and C are DEVICE pointers owned by the caller.  C must not
  * overlap A or B.  The library keeps no per-call state; its one allocation is
- * the workspace of the split-K path for few rows of A (variant
- * skinny_64x128_w4_k32_s4_splitk when it splits K over workgroups): one
- * device buffer per (device, stream), allocated with hipMalloc by the first
- * call on that stream that needs it and replaced by a larger one (at least
- * twice the size) when a later call needs more.  No buffer is freed before
- * the process exits; each is at most 256 MiB.  Calls on one stream use it in
- * stream order; calls on different streams never share one.  A call made
- * while its stream is being captured into a graph, or one whose allocation
- * fails, runs the same kernel without splitting K, which needs no
- * workspace -- so a captured graph never refers to a library buffer.
+ * a workspace used by two paths:
+ *   - the split-K path for few rows of A (variant
+ *     skinny_64x128_w4_k32_s4_splitk when it splits K over workgroups) keeps
+ *     fp32 partial results there (at most 256 MiB);
+ *   - the repack path (variant repack_pipelined: shapes the pipelined kernels
+ *     cannot read in place -- K or N not a multiple of 8, leading dimensions,
+ *     batch strides or bases not 16-byte granular -- with at least 2^24
+ *     multiply-adds) copies A and/or B there, zero-padded and aligned
+ *     (at most 1 GiB).
+ * It is one device buffer per (device, stream), allocated with hipMalloc by
+ * the first call on that stream that needs it and replaced by a larger one
+ * (at least twice the size) when a later call needs more.  No buffer is
+ * freed before the process exits.  Calls on one stream use it in stream
+ * order; calls on different streams never share one.  A call made while its
+ * stream is being captured into a graph, or one whose allocation fails,
+ * takes a path without workspace (the skinny kernel unsplit, the guarded
+ * kernel instead of the repack) -- so a captured graph never refers to a
+ * library buffer.
  *
  * Execution: the call validates its arguments on the host, enqueues the
  * kernel(s) on `stream` (NULL = the default stream) and returns without
  * waiting.  Completion is observed by synchronising the stream.  The split-K
- * path enqueues two kernels: the K-split products, then the in-order sum of
- * their fp32 partials.
+ * path enqueues two kernels (the K-split products, then the in-order sum of
+ * their fp32 partials), the repack path up to three (the copies of A and/or
+ * B, then the product).
  *
  * Errors: nothing is launched unless the status is BPT_OK.
  *   BPT_ERR_INVALID_ARG  a size or stride is negative, a leading dimension is

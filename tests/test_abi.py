@@ -131,10 +131,16 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 256, 256, 200, 200, 256) == v["pipelined_128x128x32_s4"]
     assert pkg.select_variant("f16", 1, 4096, 4096, 4104, 4104, 4096) == big
     # K % 8 != 0 (a chunk of A would straddle K), odd leading dimension,
-    # unaligned base: generic
+    # unaligned base: no pipelined kernel reads them in place.  From 2^24
+    # multiply-adds on they are copied, zero-padded and aligned, into a
+    # workspace first (256^3 is exactly 2^24); smaller ones take the guarded
+    # kernel
+    repack = v["repack_pipelined"]
     assert pkg.select_variant("f16", 1, 256, 256, 196, 196, 256) == v["generic_64x64x16"]
-    assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == v["generic_64x64x16"]
-    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == v["generic_64x64x16"]
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 260, 257) == repack
+    assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256, A_ptr=FAKE + 2) == repack
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4090, 4090, 4096) == repack
+    assert pkg.select_variant("f16", 1, 100, 70, 50, 50, 70) == v["generic_64x64x16"]
     # K = 64 is one 64-wide tile (two stages need two) and two 32-wide tiles
     # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
@@ -150,9 +156,12 @@ def test_automatic_variant_choice():
     # ... and neither when K is too short for either ring (8192 / 128 = 64
     # wide blocks, K = 768 one split only; narrow needs K >= 1024)
     assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) not in (wide, narrow)
-    # N % 8 != 0: column chunks would straddle N, so only the guarded kernel
-    assert pkg.select_variant("f16", 1, 64, 8190, 8192, 8192, 8192) == v["generic_64x64x16"]
-    assert pkg.select_variant("f16", 1, 4096, 4092, 4096, 4096, 4096) == v["generic_64x64x16"]
+    # N % 8 != 0: column chunks would straddle N in place, so the operands are
+    # repacked (B to a width of 8192 resp. 4096, C stored at the true N)
+    assert pkg.select_variant("f16", 1, 64, 8190, 8192, 8192, 8190) == repack
+    assert pkg.select_variant("f16", 1, 4096, 4092, 4096, 4096, 4092) == repack
+    # ... unless K is too short for any ring even after padding
+    assert pkg.select_variant("f16", 1, 4096, 4092, 96, 96, 4092) == v["generic_64x64x16"]
     # rejected / nothing to do
     assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0
     assert pkg.select_variant("f16", 1, 16, 16, 16, 8, 16) == 0

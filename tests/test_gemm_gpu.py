@@ -66,7 +66,7 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
             "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
-            "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk"]
+            "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk", "repack_pipelined"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
 # least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
 # aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
@@ -95,7 +95,17 @@ SHAPES_SKINNY = [(64, 1024, 2048), (37, 320, 2560), (100, 256, 2048), (1, 512, 4
 SHAPES_WIDE_ONLY = [(64, 1024, 512), (3, 136, 640)]
 
 
+# the repack route copies A and B zero-padded to K, N rounded up to 8 with
+# aligned rows, then runs a pipelined kernel: odd N (201, 65, 1000, 7), odd
+# K (129 -> 136 gives four 32-wide tiles and a tail; 250 -> 256), tight
+# (odd) leading dimensions throughout
+SHAPES_REPACK = [(300, 201, 256), (257, 65, 129), (129, 129, 250), (64, 1000, 1000), (1, 7, 130),
+                 (96, 201, 256), (512, 512, 512)]
+
+
 def _shapes(vname):
+    if vname == "repack_pipelined":
+        return SHAPES_REPACK
     if vname.startswith("skinny_64x128"):
         return SHAPES_SKINNY + SHAPES_WIDE_ONLY
     if vname.startswith("skinny"):
@@ -149,7 +159,8 @@ def test_identity_and_permutation_exact():
 
 
 PADDED_CASES = [(v, 70, 200, 2048) if v.startswith("skinny") else (v, 300, 200, 192) for v in VARIANTS] + \
-    [("generic_64x64x16", 300, 201, 200)] + [(v, 300, 200, 200) for v in TAIL_VARIANTS]
+    [("generic_64x64x16", 300, 201, 200)] + [(v, 300, 200, 200) for v in TAIL_VARIANTS] + \
+    [("repack_pipelined", 300, 201, 250)]
 
 
 @pytest.mark.parametrize("vname,M,N,K", PADDED_CASES)
@@ -258,6 +269,85 @@ def test_graph_capture_of_a_split_k_call():
         eager = pkg.gemm_f16(Ad, Bd, out_fp32=True)
         torch.cuda.synchronize()
         assert torch.equal(eager.cpu(), ref), rep
+
+
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("bf16", True)])
+def test_repack_unaligned_bases(dtype, out_fp32):
+    """Views that start one element into their storage (2-byte aligned bases)
+    and have odd row strides: the automatic choice copies them into aligned,
+    zero-padded buffers and runs the pipelined kernel; C is a view too."""
+    M, N, K = 384, 263, 520
+    Af = inputs.uniform((M, K + 3), 7601, dtype=dtype, nonzero=True)
+    Bf = inputs.uniform((K, N + 5), 7602, dtype=dtype, nonzero=True)
+    A, B = Af[:, 1:K + 1], Bf[:, 3:N + 3]
+    assert pkg.select_variant(dtype, 1, M, N, K, K + 3, N + 5, out_fp32, A_ptr=(1 << 20) + 2) == \
+        pkg.variants()["repack_pipelined"]
+    out_t = torch.float32 if out_fp32 else (torch.float16 if dtype == "f16" else torch.bfloat16)
+    Cf = torch.full((M, N + 1), 5.0, dtype=out_t, device=DEV)
+    pkg.gemm_ex(Af.to(DEV)[:, 1:K + 1], Bf.to(DEV)[:, 3:N + 3], Cf[:, 1:], dtype=dtype, out_fp32=out_fp32)
+    torch.cuda.synchronize()
+    Cf = Cf.cpu()
+    assert torch.all(Cf[:, 0] == 5.0)
+    ref = oracle.gemm(inputs.bits(A.contiguous()), inputs.bits(B.contiguous()), dtype)
+    m = oracle.compare(Cf[:, 1:].float().numpy(), ref, K)
+    assert m["ok"], m
+
+
+def test_repack_full_size_odd_shape():
+    """4000 x 4095 x 4090 (odd N and K, tight leading dimensions) through the
+    automatic choice: sampled against the oracle, random and exact-integer."""
+    M, N, K = 4000, 4095, 4090
+    assert pkg.select_variant("f16", 1, M, N, K, K, N) == pkg.variants()["repack_pipelined"]
+    b, r, c = _sample_positions(1, M, N, 2048, 23)
+    for kind in ("random", "exact"):
+        if kind == "random":
+            A = inputs.uniform((M, K), 7701, nonzero=True)
+            B = inputs.uniform((K, N), 7702, nonzero=True)
+        else:
+            A = inputs.small_integers((M, K), 7703)
+            B = inputs.small_integers((K, N), 7704)
+        say(f"[repack full] {kind}")
+        C = pkg.gemm_f16(A.to(DEV), B.to(DEV), out_fp32=(kind == "exact"))
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(C).all().item())
+        got = C[torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV)].cpu()
+        ref = oracle.gemm_at(inputs.bits(A), inputs.bits(B), b, r, c, "f16")
+        if kind == "random":
+            m = oracle.compare(got.float().numpy(), ref, K)
+            assert m["ok"], m
+        else:
+            assert np.array_equal(got.numpy(), ref)
+
+
+def test_graph_capture_of_a_repack_call():
+    """Under graph capture the repack route may not use its workspace, so the
+    guarded kernel takes the call; every replay must still be exact."""
+    M, N, K = 512, 511, 520
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["repack_pipelined"]
+    A = inputs.small_integers((M, K), 7801)
+    B = inputs.small_integers((K, N), 7802)
+    ref = torch.from_numpy(oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"))
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pkg.gemm_f16(Ad, Bd, C, out_fp32=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkg.gemm_f16(Ad, Bd, C, out_fp32=True)
+    for rep_i in range(3):
+        C.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.cpu(), ref), rep_i
+        eager = pkg.gemm_f16(Ad, Bd, out_fp32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.cpu(), ref), rep_i
 
 
 def test_split_k_workspace_streams_and_growth():
