@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex",
+    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt",
     "variants", "select_variant", "LIB_PATH",
 ]
 
@@ -47,10 +47,13 @@ def lib() -> ctypes.CDLL:
     L.gemm_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ci, p]
     L.gemm_batched_f16.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, p]
     L.gemm_ex.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
-    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex):
+    L.gemm_ex_bt.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
+    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex, L.gemm_ex_bt):
         fn.restype = ci
     L.bpt_select_variant.argtypes = [ci, i64, i64, i64, i64, p, i64, p, i64, ci]
     L.bpt_select_variant.restype = ci
+    L.bpt_select_variant_bt.argtypes = [ci, i64, i64, i64, i64, p, i64, p, i64, ci]
+    L.bpt_select_variant_bt.restype = ci
     L.bpt_variant_count.argtypes = []
     L.bpt_variant_count.restype = ci
     L.bpt_variant_name.argtypes = [ci]
@@ -133,6 +136,34 @@ def gemm_ex(A, B, C=None, *, dtype: str = "f16", out_fp32: bool = False, variant
     return C
 
 
+def gemm_ex_bt(A, Bt, C=None, *, dtype: str = "f16", out_fp32: bool = False, variant: int = 0,
+               stream=None):
+    """C = A @ Bt^T through gemm_ex_bt.  A (M,K) or (b,M,K), Bt (N,K) or
+    (b,N,K) -- B given transposed; C is allocated when None.  Returns C."""
+    torch = _torch()
+    want = torch.float16 if dtype == "f16" else torch.bfloat16
+    if A.dtype != want or Bt.dtype != want:
+        raise TypeError(f"A and Bt must be {want}, got {A.dtype} and {Bt.dtype}")
+    if not (A.is_cuda and Bt.is_cuda):
+        raise ValueError("A and Bt must be device tensors")
+    M, K, lda, sA, bA = _mat(A, "A")
+    N, K2, ldbt, sB, bB = _mat(Bt, "Bt")
+    if K2 != K or bA != bB:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)} Bt {tuple(Bt.shape)}")
+    out_t = torch.float32 if out_fp32 else want
+    if C is None:
+        shape = (M, N) if A.dim() == 2 else (bA, M, N)
+        C = torch.empty(shape, dtype=out_t, device=A.device)
+    if C.dtype != out_t:
+        raise TypeError(f"C must be {out_t}, got {C.dtype}")
+    Mc, Nc, ldc, sC, bC = _mat(C, "C")
+    if (Mc, Nc, bC) != (M, N, bA):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(bA, M, N)}")
+    _check(lib().gemm_ex_bt(_DT[dtype], bA, M, N, K, A.data_ptr(), lda, sA, Bt.data_ptr(), ldbt, sB,
+                            C.data_ptr(), ldc, sC, int(out_fp32), int(variant), _stream_handle(stream)))
+    return C
+
+
 def gemm_f16(A, B, C=None, *, out_fp32: bool = False, stream=None):
     """fp16 C = A @ B through gemm_f16 (2-D tensors)."""
     torch = _torch()
@@ -191,7 +222,8 @@ def gemm_batched_f16(A, B, C=None, *, out_fp32: bool = False, stream=None):
 
 
 def select_variant(dtype: str, batch: int, M: int, N: int, K: int, lda: int, ldb: int,
-                   out_fp32: bool = False, A_ptr: int = 0, B_ptr: int = 0) -> int:
-    """Variant id the automatic choice would run (0: rejected / nothing to do)."""
-    return int(lib().bpt_select_variant(_DT[dtype], batch, M, N, K, A_ptr or 256, lda, B_ptr or 256, ldb,
-                                        int(out_fp32)))
+                   out_fp32: bool = False, A_ptr: int = 0, B_ptr: int = 0, bt: bool = False) -> int:
+    """Variant id the automatic choice would run (0: rejected / nothing to do).
+    bt: for gemm_ex_bt (B given transposed, ldb is then Bt's leading dimension)."""
+    fn = lib().bpt_select_variant_bt if bt else lib().bpt_select_variant
+    return int(fn(_DT[dtype], batch, M, N, K, A_ptr or 256, lda, B_ptr or 256, ldb, int(out_fp32)))

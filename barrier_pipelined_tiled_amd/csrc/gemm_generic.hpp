@@ -19,8 +19,9 @@ struct GenericArgs {
 };
 
 // 64x64 output tile, 4 waves in 2x2, K-step 16.  LDS holds A as [m][k] and B
-// transposed as [n][k] so that each lane's 8 k-values are contiguous.
-template <typename T, typename OutT>
+// transposed as [n][k] so that each lane's 8 k-values are contiguous.  BT:
+// B is given transposed (N x K row-major, ldb >= K), C = A * B^T.
+template <typename T, typename OutT, bool BT = false>
 __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericArgs args) {
     typedef typename Mfma<T>::frag_t frag_t;
     constexpr int BMg = 64, BNg = 64, BKg = 16, PAD = 8;
@@ -45,9 +46,15 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(GenericArgs args) {
             int r = e / BKg, c = e % BKg;                  // A: row r, k c
             long long gm = m0 + r, gk = k0 + c;
             As[r][c] = (gm < args.M && gk < args.K) ? Ab[gm * args.lda + gk] : zero;
-            int kb = e / BNg, nb = e % BNg;                // B: k kb, col nb
-            long long bk = k0 + kb, bn = n0 + nb;
-            Bs[nb][kb] = (bk < args.K && bn < args.N) ? Bb[bk * args.ldb + bn] : zero;
+            if constexpr (BT) {
+                int nb = e / BKg, kb = e % BKg;            // Bt: row (col of C) nb, k kb
+                long long bk = k0 + kb, bn = n0 + nb;
+                Bs[nb][kb] = (bk < args.K && bn < args.N) ? Bb[bn * args.ldb + bk] : zero;
+            } else {
+                int kb = e / BNg, nb = e % BNg;            // B: k kb, col nb
+                long long bk = k0 + kb, bn = n0 + nb;
+                Bs[nb][kb] = (bk < args.K && bn < args.N) ? Bb[bk * args.ldb + bn] : zero;
+            }
         }
         __syncthreads();
         frag_t a = *(const frag_t*)&As[wm * 32 + (lane % 32)][8 * (lane / 32)];

@@ -105,7 +105,10 @@ __device__ inline int swz_b(int k) {
     return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0);
 }
 
-template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT>
+// BT: B is given transposed, N x K row-major (C = A * B^T).  Its tiles are
+// then K-contiguous like A's: copied and swizzled as A, read with
+// ds_read_b128 straight into the MFMA operand, no transposing read.
+template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT, bool BT = false>
 struct PipelinedGemm {
     static_assert(WM * WN == 4, "four waves per workgroup");
     static_assert(BK == 64 || BK == 32, "A swizzles exist for 32- and 64-wide K tiles");
@@ -116,7 +119,7 @@ struct PipelinedGemm {
     static constexpr int NB = TN / 32;          // 32x32 blocks per wave (n)
     static constexpr int KS = BK / 16;          // MFMA k-steps per tile
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(BN >= 128, "B swizzle needs >= 16 chunks per row");
+    static_assert(BT || BN >= 128, "B swizzle needs >= 16 chunks per row");
     static_assert(KS % 2 == 0, "fragment double-buffering alternates sets per k-step");
 
     static constexpr int A_STAGE = BM * BK;     // halves
@@ -130,14 +133,15 @@ struct PipelinedGemm {
     static constexpr int LPS = A_INST_W + B_INST_W;         // vmcnt units per stage per wave
     static constexpr int A_CHUNKS = BK / 8;                 // 16-byte chunks per A row
     static constexpr int A_ROWS_PER_INST = 64 / A_CHUNKS;
-    static constexpr int B_CHUNKS = BN / 8;
+    static constexpr int B_CHUNKS = BT ? BK / 8 : BN / 8;   // 16-byte chunks per B tile row
     static constexpr int B_ROWS_PER_INST = 64 / B_CHUNKS;
     static_assert(A_STAGE % 2048 == 0 && B_STAGE % 2048 == 0, "stage must split evenly over 4 waves");
     static_assert(LPS * STAGES < 64, "vmcnt is 6 bits");
 
-    // per k-step: MFMAs, LDS reads (A fragments + two B half-fragments each)
+    // per k-step: MFMAs, LDS reads (A fragments + B fragments: two transposing
+    // half-reads each, or one read when B is given transposed)
     static constexpr int NMMA = MB * NB;
-    static constexpr int NREAD = MB + 2 * NB;
+    static constexpr int NREAD = MB + (BT ? 1 : 2) * NB;
     static constexpr int RPM = (NREAD + (NMMA / 2) - 1) / (NMMA / 2);   // reads per MFMA
     // copies of one group are spread over the KS k-steps of a tile: DSLICE per
     // k-step, one every DEVERY MFMA slots, starting DOFF slots in
@@ -163,9 +167,9 @@ struct PipelinedGemm {
     typedef typename Mfma<T>::frag_t frag_t;
 };
 
-template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT>
+template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT, bool BT = false>
 __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
-    typedef PipelinedGemm<T, BM, BN, BK, STAGES, WM, WN, OutT> G;
+    typedef PipelinedGemm<T, BM, BN, BK, STAGES, WM, WN, OutT, BT> G;
     typedef typename G::frag_t frag_t;
     constexpr int MB = G::MB, NB = G::NB, LPS = G::LPS;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
@@ -192,8 +196,10 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     // ---- a3: descriptors once, per-lane offsets once -------------------------
     // Extent of each operand in bytes: anything at or beyond reads as zero.
     const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
-    const int NB_ = args.nb;               // host: NB_ % 8 == 0, N <= NB_ <= ldb
-    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + NB_) * 2));
+    const int NB_ = args.nb;               // host: NB_ % 8 == 0, N <= NB_ <= ldb (not BT)
+    // BT: B's resource starts at row n0 of B^T, so rows past N read as zero
+    const int4_t rsB = BT ? make_rsrc(Bb + (long long)n0 * ldb, (uint32_t)(((N - n0 - 1) * (long long)ldb + K) * 2))
+                          : make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + NB_) * 2));
 
     uint32_t voffA[G::A_INST_W];
 #pragma unroll
@@ -209,13 +215,18 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < G::B_INST_W; ++i) {
         int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
-        int chunk = (lane % G::B_CHUNKS) ^ swz_b(row);
-        int col = n0 + chunk * 8;
-        if (col >= NB_) col = NB_ - 8;
-        voffB[i] = (uint32_t)((row * ldb + col) * 2);
+        if constexpr (BT) {                // row = column of C, chunks along k
+            int chunk = (lane % G::B_CHUNKS) ^ swz_a<BK>(row);
+            voffB[i] = (uint32_t)((row * ldb + chunk * 8) * 2);
+        } else {
+            int chunk = (lane % G::B_CHUNKS) ^ swz_b(row);
+            int col = n0 + chunk * 8;
+            if (col >= NB_) col = NB_ - 8;
+            voffB[i] = (uint32_t)((row * ldb + col) * 2);
+        }
     }
     const uint32_t a_step = BK * 2;                        // bytes per K-tile
-    const uint32_t b_step = (uint32_t)BK * ldb * 2;
+    const uint32_t b_step = BT ? (uint32_t)BK * 2 : (uint32_t)BK * ldb * 2;
 
     // LDS read offsets (bytes, within a stage) for the MFMA operands.
     // A block mb, k-step ks: row wm*TM + mb*32 + lane%32, k ks*16 + 8*(lane/32).
@@ -237,6 +248,15 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         int col = wn * G::TN + nb * 32 + 16 * (g % 2) + 4 * (j % 4);
         int chunk = (col / 8) ^ swz_b(krow);
         rdB[nb] = (uint32_t)(G::A_STAGE * 2 + krow * BN * 2 + chunk * 16 + (col % 8) * 2);
+    }
+    // BT: B block nb, k-step ks is read like A: row (column of C) wn*TN +
+    // nb*32 + lane%32 of the [BN][BK] tile, k ks*16 + 8*(lane/32)
+    uint32_t rdBt[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        int row = wn * G::TN + (lane % 32);
+        int chunk = (ks * 2 + lane / 32) ^ swz_a<BK>(row);
+        rdBt[ks] = (uint32_t)(G::A_STAGE * 2 + (row * BK + chunk * 8) * 2);
     }
 
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
@@ -262,13 +282,16 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
 
     // Operand fragments of one k-step, double-buffered: set 0 and set 1.
     frag_t fa[2][MB];
-    short4_t fbl[2][NB], fbh[2][NB];
+    short4_t fbl[2][NB], fbh[2][NB];       // B as two transposing half-reads
+    frag_t fbt[2][NB];                     // BT: B in one read
 
     // LDS read number p (0 .. NREAD-1) of k-step ks of ring stage st into set s
     auto read_piece = [&](int st, int ks, int p, int s) __attribute__((always_inline)) {
         BPT_LDS char* sbase = lds + st * G::STAGE_BYTES;
         if (p < MB) {
             fa[s][p] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + p * 32 * BK * 2);
+        } else if constexpr (BT) {
+            fbt[s][p - MB] = *(BPT_LDS frag_t*)(sbase + rdBt[ks] + (p - MB) * 32 * BK * 2);
         } else {
             const int nb = (p - MB) / 2, h = (p - MB) % 2;
             BPT_LDS short4_t* q = (BPT_LDS short4_t*)(sbase + rdB[nb] + ks * 16 * BN * 2 + h * 4 * BN * 2);
@@ -293,8 +316,12 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
                     if (q * G::RPM + r < G::NREAD) read_piece(rst, rks, q * G::RPM + r, s ^ 1);
             }
             const int mb = q / NB, nb = q % NB;
-            frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb],
-                                                                          0, 1, 2, 3, 4, 5, 6, 7));
+            frag_t b;
+            if constexpr (BT)
+                b = fbt[s][nb];
+            else
+                b = __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb],
+                                                                       0, 1, 2, 3, 4, 5, 6, 7));
             acc[mb][nb] = Mfma<T>::mma32(b, fa[s][mb], acc[mb][nb]);
             if (dma) {
 #pragma unroll
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
         if (ktail != 0) {
             const uint32_t tbase = lds0 + STAGES * G::STAGE_BYTES;
             const uint32_t tkA = (uint32_t)(nk * BK * 2);
-            const uint32_t tkB = (uint32_t)nk * BK * ldb * 2;
+            const uint32_t tkB = BT ? tkA : (uint32_t)nk * BK * ldb * 2;
             constexpr uint32_t kPast = 0x80000000u;        // beyond any extent the host allows
 #pragma unroll
             for (int i = 0; i < G::A_INST_W; ++i) {
@@ -347,8 +374,12 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
 #pragma unroll
             for (int i = 0; i < G::B_INST_W; ++i) {
                 int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
-                dma16(rsB, tbase + G::A_STAGE * 2 + (wave * G::B_INST_W + i) * 1024,
-                      row < ktail ? voffB[i] : kPast, tkB);
+                bool valid;
+                if constexpr (BT)                          // chunks of 8 k values, as for A
+                    valid = ((lane % G::B_CHUNKS) ^ swz_a<BK>(row)) * 8 < ktail;
+                else                                       // rows of k
+                    valid = row < ktail;
+                dma16(rsB, tbase + G::A_STAGE * 2 + (wave * G::B_INST_W + i) * 1024, valid ? voffB[i] : kPast, tkB);
             }
         }
     }

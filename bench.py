@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="0 = automatic choice")
     ap.add_argument("--sleep", type=float, default=5.0, help="pause before timing (s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
+                    help="kn: B is K x N (the workloads' layout); nt: the same B handed over "
+                         "transposed (N x K) through gemm_ex_bt")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,7 +134,8 @@ def main():
         if j == 0:
             A0, B0 = A, B
         As.append(A.to(dev) if A is not None else As[0])
-        Bs.append(B.to(dev))
+        Bd = B.to(dev)
+        Bs.append(Bd.transpose(-1, -2).contiguous() if args.b_layout == "nt" else Bd)
         out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
         Cs.append(torch.empty(w.c_shape(), dtype=out_t, device=dev))
     torch.cuda.synchronize()
@@ -139,10 +143,12 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    nt = args.b_layout == "nt"
+
     def step(i):
         j = i % R
-        pkg.gemm_ex(As[j], Bs[j], Cs[j], dtype=w.dtype, out_fp32=w.out_fp32, variant=args.variant,
-                    stream=stream)
+        gemm = pkg.gemm_ex_bt if nt else pkg.gemm_ex
+        gemm(As[j], Bs[j], Cs[j], dtype=w.dtype, out_fp32=w.out_fp32, variant=args.variant, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -192,7 +198,8 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None}
 
-    variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.N, w.out_fp32)
+    variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.K if nt else w.N,
+                                                    w.out_fp32, bt=nt)
     names = {v: k for k, v in pkg.variants().items()}
     roof["traffic"] = measured_traffic(w.name, names.get(variant_id, ""))
 
@@ -201,7 +208,8 @@ def main():
         cpu = cpu_baseline(w, A0, B0)
 
     out = {
-        "metric": METRIC if w.name == "f16_4096" else f"{w.name} TFLOPS (1 MI355X)",
+        "metric": (METRIC if w.name == "f16_4096" and not nt else
+                   f"{w.name}{' with B given transposed (N x K)' if nt else ''} TFLOPS (1 MI355X)"),
         "value": value,
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -216,6 +224,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "in": w.dtype, "out": "fp32" if w.out_fp32 else w.dtype, "accumulate": "fp32",
                    "rotating_buffers": R, "kernel": names.get(variant_id, str(variant_id)),
+                   "b_layout": "N x K (transposed)" if nt else "K x N",
                    "pct_of_dense_peak": 100.0 * value / PEAK_MFMA_F16_TFLOPS},
         "roofline": roof,
         "cpu_baseline": cpu,

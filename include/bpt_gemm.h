@@ -113,12 +113,35 @@ bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                    void *C, int64_t ldc, int64_t strideC,
                    int out_fp32, int variant, struct ihipStream_t *stream);
 
+/* B given transposed: C (M x N) <- A * Bt^T, where Bt is N x K row major
+ * with leading dimension ldbt >= max(1, K) and batch stride strideBt (B is
+ * read as B[k][n] = Bt[n][k]).  This is the layout in which the pages' GEMM
+ * keeps B for its "gather" kernel (its B[N,K]); the K-contiguous rows need
+ * no transpose on the way to the matrix cores.  Everything else -- dtype,
+ * batch, out_fp32, stream, errors, degenerate shapes -- as gemm_ex.
+ * variant: 0 chooses automatically among the variants named
+ * "pipelined_bt_*" and "generic_bt_*" (fast path: A and Bt 16-byte aligned,
+ * lda, ldbt and the batch strides multiples of 8, K >= 128 and either a
+ * multiple of 32 or of 8 with a tail; any N), which are the only ones this
+ * entry point takes; the others are for gemm_ex and are rejected here with
+ * BPT_ERR_UNSUPPORTED, and vice versa. */
+bpt_status gemm_ex_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda, int64_t strideA,
+                      const void *Bt, int64_t ldbt, int64_t strideBt,
+                      void *C, int64_t ldc, int64_t strideC,
+                      int out_fp32, int variant, struct ihipStream_t *stream);
+
 /* Which variant gemm_ex(variant = 0) would run for these arguments (the
  * pointers are only inspected for alignment).  Returns 0 when the call
  * would be rejected or launch nothing. */
 int bpt_select_variant(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                        const void *A, int64_t lda, const void *B, int64_t ldb,
                        int out_fp32);
+
+/* The same for gemm_ex_bt (Bt is N x K with leading dimension ldbt). */
+int bpt_select_variant_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, const void *Bt, int64_t ldbt,
+                          int out_fp32);
 
 /* Number of variants and the name of variant v (1-based); NULL if out of
  * range.  Names spell the tile shape, K-tile and stage count. */

@@ -165,3 +165,30 @@ def test_automatic_variant_choice():
     # rejected / nothing to do
     assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0
     assert pkg.select_variant("f16", 1, 16, 16, 16, 8, 16) == 0
+
+
+def test_bt_layout_entry_point(L):
+    """gemm_ex_bt: Bt's leading dimension is checked against K, and each
+    layout rejects the other's forced variants (no launch happens)."""
+    v = pkg.variants()
+    # ldbt < K
+    st = L.gemm_ex_bt(0, 1, 64, 64, 128, FAKE, 128, 0, FAKE, 100, 0, FAKE, 64, 0, 0, 0, None)
+    assert st == pkg.BPT_ERR_INVALID_ARG
+    # ldbt >= K but < N is fine for this layout; a B-as-K x N variant is not
+    st = L.gemm_ex_bt(0, 1, 256, 512, 128, FAKE, 128, 0, FAKE, 128, 0, FAKE, 512, 0, 0,
+                      v["pipelined_256x256x32_s4"], None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+    st = L.gemm_ex(0, 1, 256, 256, 128, FAKE, 128, 0, FAKE, 256, 0, FAKE, 256, 0, 0,
+                   v["pipelined_bt_256x256x32_s4"], None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+    # automatic choice for the transposed layout
+    # 64-wide K-tiles when K allows them (whole 128-byte rows per copy) ...
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x64_s2"]
+    # ... and N need not be a multiple of 8 here
+    assert pkg.select_variant("f16", 1, 4096, 4095, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x64_s2"]
+    # K = 4104: no 64-wide tiling, the 32-wide one with a tail
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4104, 4104, 4104, bt=True) == v["pipelined_bt_256x256x32_s4"]
+    assert pkg.select_variant("f16", 1, 256, 200, 256, 256, 256, bt=True) == v["pipelined_bt_128x128x32_s4"]
+    # odd K and odd leading dimensions: the guarded kernel
+    assert pkg.select_variant("f16", 1, 300, 201, 250, 250, 250, bt=True) == v["generic_bt_64x64x16"]
+

@@ -449,3 +449,118 @@ def test_full_size_exact_integers(name):
         assert np.array_equal(got.numpy(), ref)
     else:
         assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
+
+
+# ----------------------------------------------------------------------------
+# B given transposed (gemm_ex_bt): C = A * Bt^T, Bt N x K row-major.  The
+# oracle takes B = Bt^T, transposed on the host (16-bit patterns, exact).
+# ----------------------------------------------------------------------------
+
+BT_VARIANTS = ["pipelined_bt_256x256x32_s4", "pipelined_bt_128x128x32_s4", "generic_bt_64x64x16",
+               "pipelined_bt_256x256x64_s2"]
+# any N (rows of Bt past N read as zero): 201, 7 and 520 are not multiples
+# of 8; K tails of 8 (136 = 4 x 32 + 8, 1032) as on the other layout
+SHAPES_BT = [(256, 256, 256), (300, 201, 192), (33, 520, 136), (129, 136, 256), (512, 384, 1032), (1, 7, 128)]
+SHAPES_BT_GENERIC_ONLY = [(5, 3, 1), (257, 65, 129), (100, 70, 50)]
+
+
+def _bt_shapes(vname):
+    if vname.startswith("generic"):
+        return SHAPES_BT + SHAPES_BT_GENERIC_ONLY
+    if "x64_s2" in vname:                 # 64-wide K-tiles, no tail stage: K % 64 == 0, K >= 128
+        return [(M, N, K) for (M, N, K) in SHAPES_BT if K % 64 == 0] + [(200, 264, 1088)]
+    return SHAPES_BT
+
+
+def _bt_bits(Bt):
+    """16-bit patterns of B = Bt^T for the oracle."""
+    b = inputs.bits(Bt)
+    return np.ascontiguousarray(np.swapaxes(b, -1, -2))
+
+
+def run_bt(A, Bt, dtype="f16", out_fp32=False, variant=0):
+    C = pkg.gemm_ex_bt(A.to(DEV), Bt.to(DEV), None, dtype=dtype, out_fp32=out_fp32, variant=variant)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+@pytest.mark.parametrize("vname", BT_VARIANTS)
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True), ("bf16", False)])
+def test_bt_parity_random(vname, dtype, out_fp32):
+    v = pkg.variants()[vname]
+    for i, (M, N, K) in enumerate(_bt_shapes(vname)):
+        say(f"[bt random] {vname} {dtype} out_fp32={out_fp32} M={M} N={N} K={K}")
+        A = inputs.uniform((M, K), 9000 + i, dtype=dtype, nonzero=True)
+        Bt = inputs.uniform((N, K), 9100 + i, dtype=dtype, nonzero=True)
+        got = run_bt(A, Bt, dtype, out_fp32, v)
+        ref = oracle.gemm(inputs.bits(A), _bt_bits(Bt), dtype)
+        m = oracle.compare(got.float().numpy(), ref, K)
+        assert m["ok"], (M, N, K, m)
+
+
+@pytest.mark.parametrize("vname", BT_VARIANTS)
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True)])
+def test_bt_parity_exact_integers(vname, dtype, out_fp32):
+    v = pkg.variants()[vname]
+    for i, (M, N, K) in enumerate(_bt_shapes(vname)):
+        say(f"[bt exact] {vname} {dtype} out_fp32={out_fp32} M={M} N={N} K={K}")
+        A = inputs.small_integers((M, K), 9200 + i, dtype=dtype)
+        Bt = inputs.small_integers((N, K), 9300 + i, dtype=dtype)
+        got = run_bt(A, Bt, dtype, out_fp32, v)
+        ref = oracle.gemm(inputs.bits(A), _bt_bits(Bt), dtype)
+        if out_fp32:
+            assert np.array_equal(got.numpy(), ref), (M, N, K)
+        else:
+            assert np.array_equal(as_bits(got), oracle.encode(ref, dtype)), (M, N, K)
+
+
+@pytest.mark.parametrize("vname", BT_VARIANTS)
+def test_bt_batched_and_padded(vname):
+    """Batched, and leading dimensions with NaN in every padding element
+    (Bt's rows padded past K, C's rows past N)."""
+    v = pkg.variants()[vname]
+    b, M, N, K = 3, 160, 200, 192
+    A = inputs.uniform((b, M, K), 9401, lo=-0.5, hi=0.5)
+    Bt = inputs.uniform((b, N, K), 9402, lo=-0.5, hi=0.5)
+    got = run_bt(A, Bt, "f16", False, v)
+    m = oracle.compare(got.float().numpy(), oracle.gemm(inputs.bits(A), _bt_bits(Bt)), K)
+    assert m["ok"], m
+    A2 = inputs.uniform((M, K), 9403, nonzero=True)
+    Bt2 = inputs.uniform((N, K), 9404, nonzero=True)
+    Ap = torch.full((M, K + 8), float("nan"), dtype=torch.float16)
+    Ap[:, :K] = A2
+    Btp = torch.full((N, K + 16), float("nan"), dtype=torch.float16)
+    Btp[:, :K] = Bt2
+    Cp = torch.full((M, N + 8), 7.0, dtype=torch.float16, device=DEV)
+    pkg.gemm_ex_bt(Ap.to(DEV)[:, :K], Btp.to(DEV)[:, :K], Cp[:, :N], variant=v)
+    torch.cuda.synchronize()
+    Cp = Cp.cpu()
+    assert torch.all(Cp[:, N:] == 7.0)
+    m = oracle.compare(Cp[:, :N].float().numpy(), oracle.gemm(inputs.bits(A2), _bt_bits(Bt2)), K)
+    assert m["ok"], m
+
+
+def test_bt_full_size_sampled_and_exact():
+    """4096^3 with B given transposed (the automatic choice), sampled against
+    the oracle: random inputs by tolerance, small integers bit for bit."""
+    M = N = K = 4096
+    assert pkg.select_variant("f16", 1, M, N, K, K, K, bt=True) == pkg.variants()["pipelined_bt_256x256x64_s2"]
+    b, r, c = _sample_positions(1, M, N, 2048, 29)
+    for kind in ("random", "exact"):
+        if kind == "random":
+            A = inputs.uniform((M, K), 9501, nonzero=True)
+            Bt = inputs.uniform((N, K), 9502, nonzero=True)
+        else:
+            A = inputs.small_integers((M, K), 9503)
+            Bt = inputs.small_integers((N, K), 9504)
+        say(f"[bt full] {kind}")
+        C = pkg.gemm_ex_bt(A.to(DEV), Bt.to(DEV), out_fp32=(kind == "exact"))
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(C).all().item())
+        got = C[torch.from_numpy(r).to(DEV), torch.from_numpy(c).to(DEV)].cpu()
+        ref = oracle.gemm_at(inputs.bits(A), _bt_bits(Bt), b, r, c, "f16")
+        if kind == "random":
+            m = oracle.compare(got.float().numpy(), ref, K)
+            assert m["ok"], m
+        else:
+            assert np.array_equal(got.numpy(), ref)
