@@ -7,9 +7,12 @@ in the caches; inputs uniform in [-1, 1) without zeros, seeded.  One "step"
 is one GEMM call (the whole hot path) on the next buffer set.
 
 Protocol (the "Xe2 ESIMD GEMM" page, "Performance testing" and "Workflow"):
-W untimed warm-up steps, a pause so the clocks settle, then exactly K timed
-steps between two device synchronisations.  The kernel time is measured with
-HIP events recorded on the stream the kernels are launched on.
+W untimed warm-up steps, a pause, then exactly K timed steps (default 1000)
+between two device synchronisations.  The kernel time is measured with HIP
+events recorded on the stream the kernels are launched on.  After the pause
+the clock takes some 20 ms of load to come back up, so short timed blocks
+read low (4096^3: 1090 TFLOP/s over 200 calls, 1190 over 1000, 1216 over
+3000 on the same box).
 
 The JSON line also carries
 * roofline: algorithmic flops (or bytes, for the memory-bound shape) per
@@ -98,7 +101,9 @@ def cpu_baseline(w, A, B, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    # 1000 timed calls: after the pause the clock needs some 20 ms to ramp up
+    # again, which a 200-call block (26 ms at 4096^3) would mostly measure
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="f16_4096")
     ap.add_argument("--variant", type=int, default=0, help="0 = automatic choice")
