@@ -71,22 +71,26 @@ def measured_traffic(workload: str, kernel: str):
     return int(round(kib * 1024))
 
 
-def cpu_baseline(w, A, B, budget_s: float = 12.0):
-    """Time the oracle on the first R rows of A times all of B (set 0)."""
+def cpu_baseline(w, A, B, budget_s: float = 15.0, min_s: float = 10.0):
+    """Time the oracle on the first R rows of A times all of B (set 0), R
+    grown until one call takes at least min_s seconds (or covers all rows)."""
     import oracle
     from barrier_pipelined_tiled_amd import inputs
     a_bits = inputs.bits(A if A.dim() == 2 else A[0])
     b_bits = inputs.bits(B if B.dim() == 2 else B[0])
     K, N = b_bits.shape
-    rows = 8
-    t0 = time.perf_counter()
-    oracle.gemm(a_bits[:rows], b_bits, w.dtype)
-    t = time.perf_counter() - t0
-    rows = int(max(8, min(a_bits.shape[0], rows * budget_s / max(t, 1e-3))))
-    log(f"cpu_baseline: oracle on {rows} rows ...")
-    t0 = time.perf_counter()
-    oracle.gemm(a_bits[:rows], b_bits, w.dtype)
-    t = time.perf_counter() - t0
+    rows_all = a_bits.shape[0]
+    rows = min(8, rows_all)
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(a_bits[:rows], b_bits, w.dtype)
+        t = time.perf_counter() - t0
+        if t >= min_s or rows == rows_all:
+            break
+        # small calls overstate the per-row cost (thread start-up), so the
+        # estimate is refined by the next, larger call
+        rows = int(max(rows + 1, min(rows_all, rows * budget_s / max(t, 1e-3))))
+        log(f"cpu_baseline: oracle on {rows} rows ...")
     flops = 2.0 * rows * N * K
     return {
         "value": flops / t / 1e12,
@@ -96,6 +100,61 @@ def cpu_baseline(w, A, B, budget_s: float = 12.0):
         "sample": f"rows 0..{rows - 1} of A ({rows}x{K}) times B ({K}x{N}), "
                   f"{w.dtype}, fp64 accumulation, {t:.1f} s",
     }
+
+
+def record_traffic(run_dir: str, path: str | None = None) -> None:
+    """Write profiles/traffic.json from one measurement run: for every
+    workload W with <run_dir>/bench_W.json (its config.kernel names the
+    variant), <run_dir>/pmc_fetch_W and <run_dir>/pmc_write_W (rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE of that bench command), plus the copy
+    calibration in <run_dir>/pmc_copy_fetch and pmc_copy_write (the calib
+    tool's "copy 256": 256 MiB read and written per dispatch)."""
+    import csv
+    import glob
+    import statistics
+
+    def per_kernel(d):
+        f = glob.glob(os.path.join(run_dir, d, "*counter_collection.csv"))
+        if len(f) != 1:
+            return None
+        vals = {}
+        with open(f[0]) as fh:
+            for r in csv.DictReader(fh):
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: (statistics.mean(v), len(v)) for k, v in vals.items()}
+
+    copy_kib = 256 * 1024
+    cf, cw = per_kernel("pmc_copy_fetch"), per_kernel("pmc_copy_write")
+    ck = [k for k in cf if k.startswith("copy_kernel")][0]
+    fetch_scale = copy_kib / cf[ck][0]
+    write_scale = copy_kib / cw[ck][0]
+    entries = {}
+    sha = kernel_source_sha()
+    for bj in sorted(glob.glob(os.path.join(run_dir, "bench_*.json"))):
+        wname = os.path.basename(bj)[len("bench_"):-len(".json")]
+        fe, wr = per_kernel(f"pmc_fetch_{wname}"), per_kernel(f"pmc_write_{wname}")
+        if not fe or not wr:
+            continue
+        with open(bj) as fh:
+            variant = json.loads(fh.read().strip().splitlines()[-1])["config"]["kernel"]
+        kernels = [{"name": k, "dispatches": fe[k][1], "fetch_kib": round(fe[k][0], 2),
+                    "write_kib": round(wr[k][0], 2)} for k in fe if k in wr]
+        entries[wname] = {"variant": variant, "source_sha": sha, "kernels": kernels}
+    out = {
+        "_comment": "HBM-side traffic per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                    "(KiB per dispatch, mean over the dispatches of a bench run), one entry per "
+                    "kernel of the call, scaled by what the same counters read for a plain copy "
+                    f"of 256 MiB (FETCH_SIZE {cf[ck][0]:.2f} KiB, WRITE_SIZE {cw[ck][0]:.2f} KiB). "
+                    "Valid only while the kernel sources hash to source_sha.",
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "entries": entries,
+    }
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(f"wrote {path}: {sorted(entries)} at source {sha}")
 
 
 def main():
@@ -112,7 +171,12 @@ def main():
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
                     help="kn: B is K x N (the workloads' layout); nt: the same B handed over "
                          "transposed (N x K) through gemm_ex_bt")
+    ap.add_argument("--record-traffic", metavar="RUN_DIR",
+                    help="write profiles/traffic.json from the counter runs in RUN_DIR and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GEMM of this library runs on a single "

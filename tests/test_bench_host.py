@@ -1,0 +1,85 @@
+"""Host-side bookkeeping of bench.py: the traffic figures it reports are the
+counter readings of a measurement run, scaled by the copy calibration, and
+are withheld once the kernel sources change.  No GPU is used."""
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _pmc(dirpath, rows):
+    os.makedirs(dirpath)
+    with open(os.path.join(dirpath, "x_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, value) in enumerate(rows):
+            f.write(f'{i},"{name}",C,{value}\n')
+
+
+def test_record_traffic_scales_and_sums(tmp_path):
+    run = tmp_path / "run"
+    run.mkdir()
+    # the copy reads and writes 256 MiB; FETCH_SIZE reads half of it
+    _pmc(run / "pmc_copy_fetch", [("copy_kernel(int4 const*)", 131072.0)] * 3)
+    _pmc(run / "pmc_copy_write", [("copy_kernel(int4 const*)", 262144.0)] * 3)
+    _pmc(run / "pmc_fetch_w1", [("k1", 100.0), ("k1", 300.0), ("k2", 10.0), ("k2", 10.0)])
+    _pmc(run / "pmc_write_w1", [("k1", 50.0), ("k1", 50.0), ("k2", 4.0), ("k2", 4.0)])
+    (run / "bench_w1.json").write_text(json.dumps({"config": {"kernel": "variant_a"}}) + "\n")
+    # a workload with a bench line but no counter runs is left out
+    (run / "bench_w2.json").write_text(json.dumps({"config": {"kernel": "variant_b"}}) + "\n")
+    out = tmp_path / "traffic.json"
+    bench.record_traffic(str(run), str(out))
+    t = json.loads(out.read_text())
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["write_scale"] == pytest.approx(1.0)
+    assert list(t["entries"]) == ["w1"]
+    e = t["entries"]["w1"]
+    assert e["variant"] == "variant_a" and e["source_sha"] == bench.kernel_source_sha()
+    k = {x["name"]: x for x in e["kernels"]}
+    assert k["k1"]["fetch_kib"] == 200.0 and k["k1"]["write_kib"] == 50.0 and k["k1"]["dispatches"] == 2
+    assert k["k2"]["fetch_kib"] == 10.0 and k["k2"]["write_kib"] == 4.0
+
+
+def test_measured_traffic_requires_matching_variant_and_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0123456789abcdef")
+    entry = {"variant": "v", "source_sha": "0123456789abcdef",
+             "kernels": [{"name": "a", "fetch_kib": 1.0, "write_kib": 2.0},
+                         {"name": "b", "fetch_kib": 3.0, "write_kib": 0.0}]}
+    (prof / "traffic.json").write_text(json.dumps(
+        {"fetch_scale": 2.0, "write_scale": 1.0, "entries": {"w": entry}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    # (1*2 + 2*1) + (3*2 + 0) KiB
+    assert bench.measured_traffic("w", "v") == 10 * 1024
+    assert bench.measured_traffic("w", "other_variant") is None
+    assert bench.measured_traffic("missing", "v") is None
+    entry["source_sha"] = "0" * 16
+    (prof / "traffic.json").write_text(json.dumps(
+        {"fetch_scale": 2.0, "write_scale": 1.0, "entries": {"w": entry}}))
+    assert bench.measured_traffic("w", "v") is None
+
+
+def test_kernel_source_sha_follows_the_sources(tmp_path, monkeypatch):
+    csrc = tmp_path / "barrier_pipelined_tiled_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "k.hip").write_text("a")
+    (csrc / "notes.txt").write_text("ignored")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h1 = bench.kernel_source_sha()
+    (csrc / "notes.txt").write_text("changed")
+    assert bench.kernel_source_sha() == h1
+    (csrc / "k.hip").write_text("b")
+    assert bench.kernel_source_sha() != h1
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
