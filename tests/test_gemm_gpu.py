@@ -377,6 +377,38 @@ def test_split_k_workspace_streams_and_growth():
         assert torch.equal(C.cpu(), lone[i]), i
 
 
+def test_split_k_repeated_and_interleaved():
+    """Many split-K calls in a row on one stream -- S = 2, 4 and 8 splits,
+    with repack calls that overwrite the shared workspace in between -- must
+    each give the lone call's result bit for bit (the partials are added in
+    split order), and that result meets the oracle."""
+    v = pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
+    shapes = [(64, 200, 1024), (64, 1024, 2048), (64, 2048, 4096)]      # S = 2, 4, 8
+    rp_A = inputs.uniform((257, 129), 7601, nonzero=True).to(DEV)
+    rp_B = inputs.uniform((129, 201), 7602, nonzero=True).to(DEV)
+    rp_ref = run(rp_A.cpu(), rp_B.cpu(), "f16", True, pkg.variants()["repack_pipelined"])
+    for i, (M, N, K) in enumerate(shapes):
+        say(f"split-K repeated M={M} N={N} K={K}")
+        A = inputs.uniform((M, K), 7611 + i, nonzero=True)
+        B = inputs.uniform((K, N), 7621 + i, nonzero=True)
+        lone = run(A, B, "f16", True, v)
+        m = oracle.compare(lone.numpy(), oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"), K)
+        assert m["ok"], m
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        outs, rps = [], []
+        for rep in range(24):
+            C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+            pkg.gemm_ex(Ad, Bd, C, out_fp32=True, variant=v)
+            outs.append(C)
+            if rep % 5 == 2:
+                rps.append(pkg.gemm_ex(rp_A, rp_B, out_fp32=True, variant=pkg.variants()["repack_pipelined"]))
+        torch.cuda.synchronize()
+        for rep, C in enumerate(outs):
+            assert torch.equal(C.cpu(), lone), (M, N, K, rep)
+        for C in rps:
+            assert torch.equal(C.cpu(), rp_ref)
+
+
 # ----------------------------------------------------------------------------
 # full workload sizes, automatic variant choice (the benchmark's launches)
 # ----------------------------------------------------------------------------
