@@ -14,8 +14,10 @@ so every run and every machine sees the same bits):
 * ``normal``: x = std * n with n ~ N(0, 1) in fp32, rounded the same way
   (``std`` is the standard deviation).
 
-The workload table below gives the five shapes the library is tested and
-measured on, with their value recipes and seeds.
+The workload table below gives the five GEMM shapes the library is tested
+and measured on, with their value recipes and seeds; ``ATTENTION`` holds the
+attention workloads (head dimension 256, the pages' SDP kernel) in the same
+form.
 """
 from __future__ import annotations
 
@@ -155,4 +157,64 @@ WORKLOADS = {
                                         {"kind": "uniform"},
                                         {"kind": "uniform", "scale": 1.0 / math.sqrt(8192)},
                                         base_seed=105, rotating=16, rotate_a=False),
+}
+
+
+@dataclass(frozen=True)
+class AttentionWorkload:
+    """One attention workload O = softmax(scale Q K^T) V: BH independent
+    (batch x head) problems of Sq query rows, Skv keys and head dimension D,
+    with Q, K, V drawn by ``recipe`` (Q with seed(j), K with seed(j) + 500,
+    V with seed(j) + 700) and scale 1/sqrt(D)."""
+    name: str
+    dtype: str
+    BH: int
+    Sq: int
+    Skv: int
+    D: int
+    out_fp32: bool
+    recipe: dict = field(default_factory=dict)
+    base_seed: int = 0
+    rotating: int = 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> int:
+        """Both products: Q K^T and P V, 2 flops per multiply-add each."""
+        return 4 * self.BH * self.Sq * self.Skv * self.D
+
+    @property
+    def compulsory_bytes(self) -> int:
+        ob = 4 if self.out_fp32 else 2
+        return self.BH * self.D * (2 * self.Sq + 4 * self.Skv + ob * self.Sq)
+
+    def seed(self, j: int) -> int:
+        return self.base_seed * 1000 + j
+
+    def _draw(self, shape, seed):
+        r = self.recipe
+        return uniform(shape, seed, lo=r.get("lo", -1.0), hi=r.get("hi", 1.0), dtype=self.dtype)
+
+    def make_q(self, j: int = 0) -> torch.Tensor:
+        return self._draw((self.BH, self.Sq, self.D), self.seed(j))
+
+    def make_k(self, j: int = 0) -> torch.Tensor:
+        return self._draw((self.BH, self.Skv, self.D), self.seed(j) + 500)
+
+    def make_v(self, j: int = 0) -> torch.Tensor:
+        return self._draw((self.BH, self.Skv, self.D), self.seed(j) + 700)
+
+
+ATTENTION = {
+    # small shape the oracle forms whole in about a second
+    "attn_f16_2x512x512x256": AttentionWorkload("attn_f16_2x512x512x256", "f16", 2, 512, 512, 256, False,
+                                                {"lo": -0.5, "hi": 0.5}, base_seed=201, rotating=2),
+    # the attention the batched 64 x 4096x256 . 256x4096 product is the first
+    # half of: 64 heads of 4096 queries and keys, head dimension 256, values
+    # as that product's operands
+    "attn_f16_64x4096x4096x256": AttentionWorkload("attn_f16_64x4096x4096x256", "f16", 64, 4096, 4096, 256,
+                                                   False, {"lo": -0.5, "hi": 0.5}, base_seed=202, rotating=2),
 }

@@ -1,4 +1,5 @@
-"""CPU oracle for the dense half-precision GEMM C = A * B.
+"""CPU oracle for the dense half-precision GEMM C = A * B, and for the
+second workload, scaled dot-product attention O = softmax(scale Q K^T) V.
 
 TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the
 benchmark's CPU-baseline leg are the only callers.  The GPU library never
@@ -10,6 +11,9 @@ adds the comparison metrics of the "Xe2 ESIMD GEMM" page, section
 "Correctness testing": look for non-finite values first, then judge the
 relative RMS error (read as the Frobenius norm of the difference over the
 Frobenius norm of the reference).
+
+Attention (``attention``) is the plain definition in fp64, row by row
+(oracle.c, oracle_attention), judged by ``compare_attention``.
 
 Inputs are numpy ``uint16`` arrays of 16-bit bit patterns (fp16 or bf16),
 2-D ``(rows, cols)`` or 3-D ``(batch, rows, cols)``, contiguous in the last
@@ -63,6 +67,9 @@ def _load():
     lib.oracle_gemm_at.restype = None
     lib.oracle_gemm_at.argtypes = [ctypes.c_int, i64, p, i64, i64, p, i64, i64,
                                    i64, p, p, p, p, p]
+    lib.oracle_attention.restype = None
+    lib.oracle_attention.argtypes = [ctypes.c_int, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
+                                     ctypes.c_double, i64, p, p, p, p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -171,6 +178,51 @@ def gemm_at(a: np.ndarray, b: np.ndarray, bidx, rows, cols, dtype: str = "f16",
     return (out32, out64) if want64 else out32
 
 
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, dtype: str = "f16",
+              rows=None, want64: bool = False):
+    """O = softmax(scale * Q K^T) V for 16-bit pattern inputs (oracle.c,
+    oracle_attention).
+
+    ``q``: (Sq, D) or (BH, Sq, D); ``k``, ``v``: (Skv, D) or (BH, Skv, D).
+    With ``rows`` None every output row is formed and the result has q's
+    shape; with ``rows = (bh_idx, row_idx)`` only those rows are, returned as
+    (n, D).  fp32 results, plus the fp64 values when ``want64``.
+    ``scale`` is taken as the fp32 value the GPU receives."""
+    two_d = q.ndim == 2
+    q3, ldq, sq = _as3d(q, "Q")
+    k3, ldk, sk = _as3d(k, "K")
+    v3, ldv, sv = _as3d(v, "V")
+    BH, Sq, D = q3.shape
+    if k3.shape[0] != BH or v3.shape[0] != BH or k3.shape[2] != D or v3.shape[2] != D \
+            or k3.shape[1] != v3.shape[1]:
+        raise ValueError(f"shape mismatch: Q {q.shape}, K {k.shape}, V {v.shape}")
+    Skv = k3.shape[1]
+    if rows is None:
+        bi = np.repeat(np.arange(BH, dtype=np.int64), Sq)
+        ri = np.tile(np.arange(Sq, dtype=np.int64), BH)
+    else:
+        bi = np.ascontiguousarray(rows[0], dtype=np.int64)
+        ri = np.ascontiguousarray(rows[1], dtype=np.int64)
+        if bi.size != ri.size:
+            raise ValueError("row index arrays differ in length")
+        if bi.size and (bi.min() < 0 or bi.max() >= BH or ri.min() < 0 or ri.max() >= Sq):
+            raise ValueError("row out of range")
+    n = bi.size
+    out32 = np.zeros((n, D), dtype=np.float32)
+    out64 = np.zeros((n, D), dtype=np.float64)
+    if n and D:
+        _load().oracle_attention(_DTYPES[dtype], Skv, D, q3.ctypes.data, ldq, sq,
+                                 k3.ctypes.data, ldk, sk, v3.ctypes.data, ldv, sv,
+                                 float(np.float32(scale)), n, bi.ctypes.data, ri.ctypes.data,
+                                 out32.ctypes.data, out64.ctypes.data)
+    if rows is None:
+        out32 = out32.reshape(BH, Sq, D)
+        out64 = out64.reshape(BH, Sq, D)
+        if two_d:
+            out32, out64 = out32[0], out64[0]
+    return (out32, out64) if want64 else out32
+
+
 # ----------------------------------------------------------------------------
 # comparison metrics
 # ----------------------------------------------------------------------------
@@ -196,6 +248,27 @@ def compare(gpu: np.ndarray, ref: np.ndarray, K: int) -> dict:
     are computed in fp64.  When the reference is identically zero, the
     relative metrics are undefined and only G == 0 passes.
     """
+    return _judge(gpu, ref, lambda absmax: max_abs_tol(K, absmax))
+
+
+# Attention outputs are convex combinations of value rows, so every error is
+# relative to the values' scale, not to a length of sum: the weights enter
+# the second product rounded to 16 bits (relative error <= 2^-11 each for
+# fp16) and the output is rounded once more, which bounds the element-wise
+# error by a few 2^-11 of max|O|.  1e-2 * max|O_ref| leaves a wide margin
+# for that and still fails a dropped term, a wrong scale or a missed
+# rescale of the running sums (each moves outputs by far more).
+ATTN_MAX_ABS_REL = 1e-2
+
+
+def compare_attention(gpu: np.ndarray, ref: np.ndarray) -> dict:
+    """Judge a GPU attention output against the oracle's: non-finite count
+    first, then rel_rms <= 5e-3 (the pages' criterion) and max|G - R| <=
+    1e-2 * max|R|."""
+    return _judge(gpu, ref, lambda absmax: ATTN_MAX_ABS_REL * absmax)
+
+
+def _judge(gpu, ref, tol_of_absmax) -> dict:
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     if g.shape != r.shape:
@@ -215,7 +288,7 @@ def compare(gpu: np.ndarray, ref: np.ndarray, K: int) -> dict:
                    max_abs_tol=0.0, ok=(max_abs == 0.0))
         return out
     rel_rms = float(np.sqrt(np.sum(diff * diff)) / rnorm)
-    tol = max_abs_tol(K, ref_absmax)
+    tol = float(tol_of_absmax(ref_absmax))
     out.update(rel_rms=rel_rms, max_abs=max_abs, max_abs_tol=tol,
                ok=bool(rel_rms <= REL_RMS_TOL and max_abs <= tol))
     return out

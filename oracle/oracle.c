@@ -23,12 +23,16 @@
  * in double (at most 11+11 significant bits), so the only rounding inside the
  * sum is fp64 addition, performed in ascending k.
  *
+ * The same file holds the reference for the second workload, scaled
+ * dot-product attention (oracle_attention, below).
+ *
  * Build: gcc -O2 -fopenmp -fPIC -shared (no -ffast-math: the summation order
  * written below must be the one executed).
  */
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ------------------------------------------------------------------ */
@@ -241,6 +245,82 @@ void oracle_gemm_at(int dtype, int64_t K,
             acc += decode(is_bf16, Ab[k]) * decode(is_bf16, Bb[k * ldb]);
         if (out32) out32[t] = (float)acc;
         if (out64) out64[t] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Scaled dot-product attention (the pages' "SDP" / flash-attention     */
+/* workload): O = softmax(scale * Q K^T) V, row by row                  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * oracle_attention: for n chosen output rows (bh[t], row[t]) of
+ *     O[b][i][d] = sum_j p_j V[b][j][d] / sum_j p_j,
+ *     p_j = exp(s_j - max_j s_j),
+ *     s_j = scale * sum_{e=0}^{D-1} Q[b][i][e] * K[b][j][e]
+ * with j over the Skv keys, no mask.  This is the plain definition of a
+ * softmax over the scaled logits followed by the weighted sum of value rows
+ * (the "Named Barriers" page, section "Proven Pattern: SDP Kernel Split
+ * Barrier B", names this kernel, an HD = 256 flash attention); subtracting
+ * the row maximum changes no exact value and keeps exp() finite.
+ *
+ * Everything is fp64: the dot products in ascending e (the products of two
+ * 16-bit values are exact), exp() from the C library, the sums over keys
+ * in ascending j, one division per output.  out32 gets the result rounded
+ * once to fp32, out64 (when not NULL) the fp64 value.  Output t is written
+ * at out[t * D + d].  Skv == 0 writes zeros (an empty softmax has no
+ * weights).  Q, K, V are 16-bit patterns, leading dimensions and batch
+ * strides in elements; scale is used as given (the GPU path receives the
+ * same value).
+ */
+void oracle_attention(int dtype, int64_t Skv, int64_t D,
+                      const uint16_t *Q, int64_t ldq, int64_t strideQ,
+                      const uint16_t *K, int64_t ldk, int64_t strideK,
+                      const uint16_t *V, int64_t ldv, int64_t strideV,
+                      double scale, int64_t n, const int64_t *bh, const int64_t *row,
+                      float *out32, double *out64)
+{
+    int is_bf16 = (dtype == 1);
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(Skv > 0 ? Skv : 1) * sizeof(double));
+        double *q = (double *)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
+        double *o = (double *)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n; ++t) {
+            const uint16_t *qrow = Q + bh[t] * strideQ + row[t] * ldq;
+            const uint16_t *Kb = K + bh[t] * strideK;
+            const uint16_t *Vb = V + bh[t] * strideV;
+            for (int64_t e = 0; e < D; ++e) q[e] = decode(is_bf16, qrow[e]);
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            if (Skv > 0) {
+                /* logits and their maximum */
+                double smax = -INFINITY;
+                for (int64_t j = 0; j < Skv; ++j) {
+                    const uint16_t *krow = Kb + j * ldk;
+                    double acc = 0.0;
+                    for (int64_t e = 0; e < D; ++e) acc += q[e] * decode(is_bf16, krow[e]);
+                    s[j] = scale * acc;
+                    if (s[j] > smax) smax = s[j];
+                }
+                /* weights, their sum, and the weighted sum of value rows */
+                double l = 0.0;
+                for (int64_t j = 0; j < Skv; ++j) {
+                    double pj = exp(s[j] - smax);
+                    l += pj;
+                    const uint16_t *vrow = Vb + j * ldv;
+                    for (int64_t d = 0; d < D; ++d) o[d] += pj * decode(is_bf16, vrow[d]);
+                }
+                for (int64_t d = 0; d < D; ++d) o[d] /= l;
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                if (out32) out32[t * D + d] = (float)o[d];
+                if (out64) out64[t * D + d] = o[d];
+            }
+        }
+        free(s);
+        free(q);
+        free(o);
     }
 }
 
