@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt",
+    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt", "attention_fwd",
     "variants", "select_variant", "LIB_PATH",
 ]
 
@@ -48,7 +48,9 @@ def lib() -> ctypes.CDLL:
     L.gemm_batched_f16.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, p]
     L.gemm_ex.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
     L.gemm_ex_bt.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
-    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex, L.gemm_ex_bt):
+    L.attention_fwd.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
+                                p, i64, i64, ctypes.c_float, ci, p]
+    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex, L.gemm_ex_bt, L.attention_fwd):
         fn.restype = ci
     L.bpt_select_variant.argtypes = [ci, i64, i64, i64, i64, p, i64, p, i64, ci]
     L.bpt_select_variant.restype = ci
@@ -162,6 +164,39 @@ def gemm_ex_bt(A, Bt, C=None, *, dtype: str = "f16", out_fp32: bool = False, var
     _check(lib().gemm_ex_bt(_DT[dtype], bA, M, N, K, A.data_ptr(), lda, sA, Bt.data_ptr(), ldbt, sB,
                             C.data_ptr(), ldc, sC, int(out_fp32), int(variant), _stream_handle(stream)))
     return C
+
+
+def attention_fwd(Q, K, V, O=None, *, scale: float | None = None, dtype: str = "f16",
+                  out_fp32: bool = False, stream=None):
+    """O = softmax(scale * Q K^T) V through attention_fwd.  Q (Sq, D) or
+    (BH, Sq, D); K, V (Skv, D) or (BH, Skv, D); scale defaults to
+    1/sqrt(D).  O is allocated when None.  Returns O."""
+    torch = _torch()
+    want = torch.float16 if dtype == "f16" else torch.bfloat16
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        if t.dtype != want:
+            raise TypeError(f"{n} must be {want}, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a device tensor")
+    Sq, D, ldq, sQ, BH = _mat(Q, "Q")
+    Skv, Dk, ldk, sK, bK = _mat(K, "K")
+    Skv2, Dv, ldv, sV, bV = _mat(V, "V")
+    if Dk != D or Dv != D or Skv2 != Skv or bK != BH or bV != BH:
+        raise ValueError(f"shape mismatch: Q {tuple(Q.shape)} K {tuple(K.shape)} V {tuple(V.shape)}")
+    out_t = torch.float32 if out_fp32 else want
+    if O is None:
+        O = torch.empty(Q.shape, dtype=out_t, device=Q.device)
+    if O.dtype != out_t:
+        raise TypeError(f"O must be {out_t}, got {O.dtype}")
+    So, Do, ldo, sO, bO = _mat(O, "O")
+    if (So, Do, bO) != (Sq, D, BH):
+        raise ValueError(f"O has shape {tuple(O.shape)}, expected {tuple(Q.shape)}")
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    _check(lib().attention_fwd(_DT[dtype], BH, Sq, Skv, D, Q.data_ptr(), ldq, sQ, K.data_ptr(), ldk, sK,
+                               V.data_ptr(), ldv, sV, O.data_ptr(), ldo, sO, float(scale), int(out_fp32),
+                               _stream_handle(stream)))
+    return O
 
 
 def gemm_f16(A, B, C=None, *, out_fp32: bool = False, stream=None):

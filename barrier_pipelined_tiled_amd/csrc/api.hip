@@ -4,6 +4,7 @@
 // variants) and the asynchronous launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -13,6 +14,7 @@
 #include <utility>
 
 #include "../../include/bpt_gemm.h"
+#include "attention.hpp"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
@@ -576,9 +578,84 @@ bpt_status run(const Call& c, int variant, hipStream_t stream) {
     return BPT_OK;
 }
 
+// ---------------------------------------------------------------------------
+// attention: O = softmax(scale Q K^T) V
+// ---------------------------------------------------------------------------
+
+struct AttnCall {
+    int dtype;
+    long long BH, Sq, Skv, D;
+    const void *Q, *K, *V;
+    void* O;
+    long long ldq, ldk, ldv, ldo, sQ, sK, sV, sO;
+    float scale;
+    int out_fp32;
+};
+
+template <typename T, typename OutT>
+hipError_t launch_attention(const AttnCall& c, hipStream_t stream) {
+    bpt::AttnArgs a;
+    a.Q = c.Q; a.K = c.K; a.V = c.V; a.O = c.O;
+    a.Sq = (int)c.Sq; a.Skv = (int)c.Skv;
+    a.ldq = (int)c.ldq; a.ldk = (int)c.ldk; a.ldv = (int)c.ldv; a.ldo = (int)c.ldo;
+    a.sQ = c.sQ; a.sK = c.sK; a.sV = c.sV; a.sO = c.sO;
+    a.c2 = (float)((double)c.scale * 1.4426950408889634);     // scale * log2(e)
+    a.q_tiles = (int)((c.Sq + 127) / 128);
+    const dim3 grid((unsigned)(a.q_tiles * c.BH));
+    if (c.D == 256)
+        hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 256, OutT>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 128, OutT>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+bpt_status attention_run(const AttnCall& c, hipStream_t stream) {
+    if (c.dtype != 0 && c.dtype != 1) return fail(BPT_ERR_INVALID_ARG, "dtype must be 0 (fp16) or 1 (bf16), got %d", c.dtype);
+    if (c.out_fp32 != 0 && c.out_fp32 != 1) return fail(BPT_ERR_INVALID_ARG, "out_fp32 must be 0 or 1, got %d", c.out_fp32);
+    if (c.BH < 0 || c.Sq < 0 || c.Skv < 0 || c.D < 1)
+        return fail(BPT_ERR_INVALID_ARG, "bad size: batch_heads=%lld seq_q=%lld seq_kv=%lld head_dim=%lld",
+                    c.BH, c.Sq, c.Skv, c.D);
+    if (c.ldq < c.D || c.ldk < c.D || c.ldv < c.D || c.ldo < c.D)
+        return fail(BPT_ERR_INVALID_ARG, "a leading dimension is below head_dim=%lld (ldq=%lld ldk=%lld ldv=%lld ldo=%lld)",
+                    c.D, c.ldq, c.ldk, c.ldv, c.ldo);
+    if (c.sQ < 0 || c.sK < 0 || c.sV < 0 || c.sO < 0)
+        return fail(BPT_ERR_INVALID_ARG, "negative stride: %lld %lld %lld %lld", c.sQ, c.sK, c.sV, c.sO);
+    if (!std::isfinite(c.scale)) return fail(BPT_ERR_INVALID_ARG, "scale is not finite");
+    if (c.BH == 0 || c.Sq == 0) return BPT_OK;
+    if (c.Q == nullptr || c.O == nullptr) return fail(BPT_ERR_INVALID_ARG, "Q or O is NULL");
+    if (c.Skv > 0 && (c.K == nullptr || c.V == nullptr)) return fail(BPT_ERR_INVALID_ARG, "K or V is NULL");
+    if (c.D != 128 && c.D != 256) return fail(BPT_ERR_UNSUPPORTED, "head_dim %lld: only 128 and 256 are built", c.D);
+    if (!aligned16(c.Q) || !aligned16(c.K) || !aligned16(c.V) || !aligned16(c.O) ||
+        c.ldq % 8 || c.ldk % 8 || c.ldv % 8 || c.ldo % 8 || c.sQ % 8 || c.sK % 8 || c.sV % 8 || c.sO % 8)
+        return fail(BPT_ERR_UNSUPPORTED, "attention needs 16-byte aligned bases and leading dimensions and "
+                                         "strides that are multiples of 8 elements");
+    const long long q_tiles = (c.Sq + 127) / 128;
+    if ((c.Sq + 128) * c.ldq * 2 > kI31 || (c.Skv + 64) * c.ldk * 2 > kI31 || (c.Skv + 64) * c.ldv * 2 > kI31 ||
+        c.Sq * c.ldo > kI31 || q_tiles * c.BH > kI31)
+        return fail(BPT_ERR_UNSUPPORTED, "a head's Q, K, V or O extent, or the workgroup count, exceeds 2^31-1");
+    hipError_t e;
+    if (c.dtype == 0)
+        e = c.out_fp32 ? launch_attention<_Float16, float>(c, stream) : launch_attention<_Float16, _Float16>(c, stream);
+    else
+        e = c.out_fp32 ? launch_attention<__bf16, float>(c, stream) : launch_attention<__bf16, __bf16>(c, stream);
+    if (e != hipSuccess) return fail(BPT_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return BPT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+bpt_status attention_fwd(int dtype, int64_t batch_heads, int64_t seq_q, int64_t seq_kv, int64_t head_dim,
+                         const void* Q, int64_t ldq, int64_t strideQ,
+                         const void* K, int64_t ldk, int64_t strideK,
+                         const void* V, int64_t ldv, int64_t strideV,
+                         void* O, int64_t ldo, int64_t strideO,
+                         float scale, int out_fp32, struct ihipStream_t* stream) {
+    AttnCall c{dtype, batch_heads, seq_q, seq_kv, head_dim, Q, K, V, O,
+               ldq, ldk, ldv, ldo, strideQ, strideK, strideV, strideO, scale, out_fp32};
+    return attention_run(c, reinterpret_cast<hipStream_t>(stream));
+}
 
 bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                    const void* A, int64_t lda, int64_t strideA,

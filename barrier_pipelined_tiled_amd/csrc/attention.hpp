@@ -1,0 +1,272 @@
+// attention.hpp -- fused scaled dot-product attention, forward:
+//     O = softmax(scale * Q K^T) V
+// for BH independent (batch x head) problems of Sq query rows, Skv keys and
+// head dimension D (128 or 256), fp16 or bf16 in, fp32 accumulation.
+//
+// This is the second workload of the pages: the "Named Barriers" page
+// (section "Proven Pattern: SDP Kernel Split Barrier B") describes an
+// HD = 256 flash-attention kernel whose loop runs QK products, the softmax,
+// a trip of S through shared memory, then the PV products, with the loads of
+// V and the prefetch of the next K placed between the barrier's arrive and
+// its wait.  On gfx950 the same schedule is rebuilt as follows.
+//
+// * Workgroup: 4 waves, 128 query rows; wave w owns rows 32w .. 32w+31 and
+//   keeps its Q fragments in registers for the whole key loop.  Every
+//   softmax statistic of a row lives in that row's two lanes (l and l+32),
+//   so no reduction crosses waves -- the pages' barrier for the shared
+//   softmax maximum has nothing to do here.
+// * K and V blocks of 64 keys are staged global->LDS by LDS-DMA in a ring of
+//   two stages.  Block j is published by a vmcnt wait plus one s_barrier;
+//   right after it the copies of block j+1 are issued into the other stage
+//   (the window), and the math of block j follows.
+// * S never goes through LDS.  S^T = K Q^T is formed with K as the MFMA's
+//   row operand, so lane l holds query row l%32 and 16 keys of each 32-key
+//   half-block.  The keys a lane holds are exactly the ones its half of the
+//   wave must supply to the PV product if the key order inside each 16-key
+//   step is permuted (keys 4h..4h+3 and 8+4h..8+4h+3 for half h), and V is
+//   read from LDS with the same permutation (transposing reads of rows
+//   4h.. and 8+4h..).  So P goes from the S accumulators to the PV operand
+//   in registers: a conversion to 16 bits and nothing else.
+// * Online softmax in base 2 with a lazy rescale: the running maximum m of
+//   a row is raised (and O and the row sum l scaled by 2^(m_old - m_new))
+//   only when some row of the wave sees a logit more than 2^8 above its m;
+//   otherwise the block's weights are taken against the stale m (each at
+//   most 2^8).  O / l is the same either way.
+// * The last key block, when Skv is not a multiple of 64, is peeled from the
+//   loop and masks keys >= Skv to -inf; K and V rows past Skv read as zero
+//   (the buffer range check).
+#pragma once
+#include "device_common.hpp"
+#include "gemm_pipelined.hpp"   // swz_b
+
+namespace bpt {
+
+struct AttnArgs {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    int Sq, Skv;
+    int ldq, ldk, ldv, ldo;                 // row strides (elements)
+    long long sQ, sK, sV, sO;               // per (batch x head) strides (elements)
+    float c2;                               // scale * log2(e)
+    int q_tiles;                            // ceil(Sq / 128)
+};
+
+template <typename T, int D>
+struct AttnFwd {
+    static_assert(D == 128 || D == 256, "head dimensions 128 and 256");
+    static constexpr int WAVES = 4, BM = 128, BN = 64;
+    static constexpr int DC = D / 8;                    // 16-byte chunks per row
+    static constexpr int ROWS_PER_KIB = 1024 / (D * 2); // rows one wave-wide copy covers
+    static constexpr int TILE = BN * D * 2;             // one K or V block in LDS
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int COPIES = TILE / 1024 / WAVES;  // per wave per tile
+    static constexpr int TS = D / 16;                   // k-steps of Q K^T
+    static constexpr int DB = D / 32;                   // 32-wide d blocks of O
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(2 * COPIES < 64, "vmcnt");
+};
+
+// K rows are read 32 at a time at one 16-byte chunk (ds_read_b128 into the
+// MFMA row operand): chunk ^ (row & 15) spreads 16 consecutive rows over
+// all 64 banks.  V rows are read by 4-row transposing reads, for which the
+// GEMM's B swizzle (swz_b) already spreads the rows.
+__device__ inline int attn_swz_k(int row) { return row & 15; }
+
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
+    typedef AttnFwd<T, D> G;
+    typedef typename Mfma<T>::frag_t frag_t;
+    constexpr int BN = G::BN, TS = G::TS, DB = G::DB;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
+    BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;                             // half of the wave
+
+    // XCD-aware order: a run of consecutive (head, query tile) pairs -- the
+    // tiles of one head, sharing its K and V -- stays on one XCD's L2
+    int pid = blockIdx.x;
+    const int num = gridDim.x;
+    if ((num & 7) == 0) pid = (pid & 7) * (num >> 3) + (pid >> 3);
+    const int bh = pid / a.q_tiles;
+    const int q0 = (pid - bh * a.q_tiles) * G::BM;
+    const int Sq = a.Sq, Skv = a.Skv;
+
+    const T* Qb = static_cast<const T*>(a.Q) + bh * a.sQ + (long long)q0 * a.ldq;
+    const T* Kb = static_cast<const T*>(a.K) + bh * a.sK;
+    const T* Vb = static_cast<const T*>(a.V) + bh * a.sV;
+
+    // ---- Q fragments: row 32w + l%32, d = 16t + 8h .. +7 (zero past Sq) ----
+    frag_t qf[TS];
+    {
+        const int rows = Sq - q0;                        // >= 1
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(Qb), 0, (int)(((long long)(rows - 1) * a.ldq + D) * 2), kBufferWord3);
+        const uint32_t vq = (uint32_t)(((wave * 32 + (lane & 31)) * a.ldq + 8 * h) * 2);
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+            qf[t] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * 32, 0, 0));
+    }
+
+    float16_t oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        oacc[db] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float m_run = -__builtin_inff();                     // running max of the row (base 2)
+    float l_half = 0.f;                                  // this half's share of the row sum
+
+    const int nblk = (Skv + BN - 1) / BN;
+    if (nblk > 0) {
+        const int4_t rsK = make_rsrc(Kb, (uint32_t)(((long long)(Skv - 1) * a.ldk + D) * 2));
+        const int4_t rsV = make_rsrc(Vb, (uint32_t)(((long long)(Skv - 1) * a.ldv + D) * 2));
+        // copies: wave w brings KiB w*COPIES + i of each tile; lane p lands at
+        // 16-byte slot p of it = row i*ROWS_PER_KIB + p/DC (of the wave's
+        // rows), physical chunk p%DC, holding logical chunk (p%DC) ^ swz(row)
+        uint32_t voffK[G::COPIES], voffV[G::COPIES];
+#pragma unroll
+        for (int i = 0; i < G::COPIES; ++i) {
+            const int row = (wave * G::COPIES + i) * G::ROWS_PER_KIB + lane / G::DC;
+            const int pc = lane % G::DC;
+            voffK[i] = (uint32_t)((row * a.ldk + 8 * (pc ^ attn_swz_k(row))) * 2);
+            voffV[i] = (uint32_t)((row * a.ldv + 8 * (pc ^ swz_b(row))) * 2);
+        }
+        const uint32_t ldsb = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+        const uint32_t kstepK = (uint32_t)(BN * a.ldk * 2), kstepV = (uint32_t)(BN * a.ldv * 2);
+        auto issue = [&](int j) __attribute__((always_inline)) {
+            const uint32_t st = ldsb + (j & 1) * G::STAGE + wave * G::COPIES * 1024;
+#pragma unroll
+            for (int i = 0; i < G::COPIES; ++i) dma16(rsK, st + i * 1024, voffK[i] + j * kstepK, 0);
+#pragma unroll
+            for (int i = 0; i < G::COPIES; ++i) dma16(rsV, st + G::TILE + i * 1024, voffV[i] + j * kstepV, 0);
+        };
+
+        // fragment reads.  K (row operand of S^T = K Q^T): key 32kb + l%32,
+        // logical chunk 2t + h, physical (2t + h) ^ (l & 15); the XOR keeps
+        // bit 4, so t >= 8 adds 256 bytes.
+        uint32_t rdK[8];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+            rdK[t8] = (uint32_t)((lane & 31) * D * 2 + (((2 * t8 + h) ^ attn_swz_k(lane)) * 16));
+        // V (row operand of O^T = V^T P^T), transposing 4-row reads: 16-lane
+        // group g, lane j reads row 4(g/2) + j/4 (+8 for the upper four keys,
+        // +16ks) at columns 32db + 16(g%2) + 4(j%4); chunk 4db + x with
+        // x = 2(g%2) + (j%4)/2, swizzled by s = swz_b(j/4):
+        // (4db + x) ^ s = 4(db ^ (s>>2)) + (x ^ (s&3)).
+        const int g = lane >> 4, jj = lane & 15;
+        const int sv = swz_b(jj >> 2);
+        const int xv = 2 * (g & 1) + ((jj & 3) >> 1);
+        uint32_t rdV[4];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4)
+            rdV[w4] = (uint32_t)((4 * (g >> 1) + (jj >> 2)) * D * 2 + 64 * (w4 ^ (sv >> 2)) +
+                                 16 * (xv ^ (sv & 3)) + 8 * (jj & 1));
+
+        auto block = [&]<bool MASK>(int j) __attribute__((always_inline)) {
+            BPT_LDS char* kt = lds + (j & 1) * G::STAGE;
+            BPT_LDS char* vt = kt + G::TILE;
+            // S^T for keys 64j .. 64j+63 (two 32-key halves)
+            float16_t s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < TS; ++t)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    frag_t kf = *(BPT_LDS frag_t*)(kt + rdK[t & 7] + (t >> 3) * 256 + kb * 32 * D * 2);
+                    s[kb] = Mfma<T>::mma32(kf, qf[t], s[kb]);
+                }
+            // logits in base 2; key of register r of half kb: 64j + 32kb +
+            // 8(r/4) + 4h + r%4
+            float mloc = -__builtin_inff();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = s[kb][r] * a.c2;
+                    if constexpr (MASK) {
+                        const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key >= Skv) x = -__builtin_inff();
+                    }
+                    s[kb][r] = x;
+                    mloc = __builtin_fmaxf(mloc, x);
+                }
+            mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32));
+            // raise the running max only when some row would otherwise see a
+            // weight above 2^8
+            if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.0f) != 0) {
+                const float m_new = __builtin_fmaxf(m_run, mloc);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_half *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            }
+            // weights, their sum, and the PV operands (keys 16ks .. 16ks+15 of
+            // the block are registers 8(ks&1) .. +7 of half ks>>1)
+            frag_t pf[4];
+            float psum = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + i] - m_run);
+                    psum += p;
+                    pf[ks][i] = (typename Mfma<T>::elem_t)p;
+                }
+            l_half += psum;
+            // O^T += V^T P^T
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    BPT_LDS char* p = vt + rdV[db & 3] + (db >> 2) * 256 + ks * 16 * D * 2;
+                    short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+                    short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 8 * D * 2));
+                    frag_t vf = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = Mfma<T>::mma32(vf, pf[ks], oacc[db]);
+                }
+        };
+
+        issue(0);
+        const bool ragged = (Skv % BN) != 0;
+        const int nfull = ragged ? nblk - 1 : nblk;
+        int j = 0;
+        for (; j < nfull; ++j) {
+            // publish block j: this wave's copies landed (vmcnt), every wave's
+            // copies landed and every wave is done with block j-1 (s_barrier)
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (j + 1 < nblk) issue(j + 1);
+            block.template operator()<false>(j);
+        }
+        if (ragged) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            block.template operator()<true>(j);
+        }
+    }
+
+    // ---- O = O / l, rows < Sq ------------------------------------------------
+    const float l_row = l_half + __shfl_xor(l_half, 32);
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const int qrow = q0 + wave * 32 + (lane & 31);
+    if (qrow < Sq) {
+        OutT* orow = static_cast<OutT*>(a.O) + bh * a.sO + (long long)qrow * a.ldo;
+        typedef OutT out4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                out4_t v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = cvt_out<OutT>(oacc[db][4 * r4 + q] * inv);
+                *(out4_t*)(orow + 32 * db + 8 * r4 + 4 * h) = v;
+            }
+    }
+}
+
+}  // namespace bpt

@@ -83,6 +83,7 @@ struct Mfma;
 
 template <>
 struct Mfma<_Float16> {
+    typedef _Float16 elem_t;
     typedef half8_t frag_t;
     __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -91,6 +92,7 @@ struct Mfma<_Float16> {
 
 template <>
 struct Mfma<__bf16> {
+    typedef __bf16 elem_t;
     typedef bf16x8_t frag_t;
     __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -131,6 +131,32 @@ bpt_status gemm_ex_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                       void *C, int64_t ldc, int64_t strideC,
                       int out_fp32, int variant, struct ihipStream_t *stream);
 
+/* Fused scaled dot-product attention, forward (the pages' second workload:
+ * the HD = 256 flash-attention "SDP" kernel of the "Named Barriers" page,
+ * section "Proven Pattern: SDP Kernel Split Barrier B"):
+ *     O[b][i][d] = sum_j p_j V[b][j][d] / sum_j p_j,
+ *     p_j = exp(s_j - max_j s_j),  s_j = scale * sum_e Q[b][i][e] K[b][j][e]
+ * for every b < batch_heads and query row i < seq_q, j over all seq_kv keys
+ * (no mask).  Q is seq_q x head_dim, K and V are seq_kv x head_dim, O is
+ * seq_q x head_dim, all row major with leading dimensions ldq, ldk, ldv,
+ * ldo (>= head_dim) and strides strideQ .. strideO (>= 0) between the
+ * batch_heads problems, in elements.  dtype: 0 = fp16, 1 = bf16 inputs; O
+ * is the input type (round to nearest even) or fp32 (out_fp32 = 1).  The
+ * logits and all sums are fp32; the weights enter the second product
+ * rounded to the input type.  scale is typically 1/sqrt(head_dim).
+ * Ownership, stream and errors as for the GEMMs; O must not overlap Q, K or
+ * V.  head_dim must be 128 or 256, the bases 16-byte aligned and the
+ * leading dimensions and strides multiples of 8 (else BPT_ERR_UNSUPPORTED);
+ * a non-finite scale is BPT_ERR_INVALID_ARG.  batch_heads == 0 or
+ * seq_q == 0 launches nothing; seq_kv == 0 writes zeros to O (an empty
+ * softmax has no weights).  No workspace is used. */
+bpt_status attention_fwd(int dtype, int64_t batch_heads, int64_t seq_q, int64_t seq_kv, int64_t head_dim,
+                         const void *Q, int64_t ldq, int64_t strideQ,
+                         const void *K, int64_t ldk, int64_t strideK,
+                         const void *V, int64_t ldv, int64_t strideV,
+                         void *O, int64_t ldo, int64_t strideO,
+                         float scale, int out_fp32, struct ihipStream_t *stream);
+
 /* Which variant gemm_ex(variant = 0) would run for these arguments (the
  * pointers are only inspected for alignment).  Returns 0 when the call
  * would be rejected or launch nothing. */
