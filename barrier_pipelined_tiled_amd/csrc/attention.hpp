@@ -21,17 +21,19 @@
 //   (the window), and the math of block j follows.
 // * S never goes through LDS.  S^T = K Q^T is formed with K as the MFMA's
 //   row operand, so lane l holds query row l%32 and 16 keys of each 32-key
-//   half-block.  The keys a lane holds are exactly the ones its half of the
-//   wave must supply to the PV product if the key order inside each 16-key
-//   step is permuted (keys 4h..4h+3 and 8+4h..8+4h+3 for half h), and V is
-//   read from LDS with the same permutation (transposing reads of rows
-//   4h.. and 8+4h..).  So P goes from the S accumulators to the PV operand
-//   in registers: a conversion to 16 bits and nothing else.
-// * Online softmax in base 2 with a lazy rescale: the running maximum m of
-//   a row is raised (and O and the row sum l scaled by 2^(m_old - m_new))
-//   only when some row of the wave sees a logit more than 2^8 above its m;
-//   otherwise the block's weights are taken against the stale m (each at
-//   most 2^8).  O / l is the same either way.
+//   half-block.  Those are exactly the keys its half of the wave must supply
+//   to the PV product if the key order inside each 16-key step is permuted
+//   (keys 4h..4h+3 and 8+4h..8+4h+3 for half h), and V is read from LDS with
+//   the same permutation (transposing reads of rows 4h.. and 8+4h..).  So P
+//   goes from the S accumulators to the PV operand in registers.
+// * Online softmax in base 2 with a lazy rescale: a row's running maximum m
+//   is raised (and its O and sum scaled by 2^(m_old - m_new)) only when some
+//   row of the wave sees a logit more than 2^8 above its m; otherwise the
+//   block's weights are taken against the stale m (each at most 2^8).  O / l
+//   is the same either way.  The rescale multiplies O where the MFMAs keep
+//   it, in the accumulation registers (read, multiply, write back per
+//   value); written as a plain multiply, it makes the compiler keep a second
+//   copy of O in ordinary registers and refresh it on every key block.
 // * The last key block, when Skv is not a multiple of 64, is peeled from the
 //   loop and masks keys >= Skv to -inf; K and V rows past Skv read as zero
 //   (the buffer range check).
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                             // half of the wave
+    const float kNegInf = -__builtin_inff();
 
     // XCD-aware order: a run of consecutive (head, query tile) pairs -- the
     // tiles of one head, sharing its K and V -- stays on one XCD's L2
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         oacc[db] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float m_run = -__builtin_inff();                     // running max of the row (base 2)
+    float m_run = kNegInf;                               // running max of the row (base 2)
     float l_half = 0.f;                                  // this half's share of the row sum
 
     const int nblk = (Skv + BN - 1) / BN;
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                 }
             // logits in base 2; key of register r of half kb: 64j + 32kb +
             // 8(r/4) + 4h + r%4
-            float mloc = -__builtin_inff();
+            float mloc = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -201,21 +204,32 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
             // weight above 2^8
             if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.0f) != 0) {
                 const float m_new = __builtin_fmaxf(m_run, mloc);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                // a row with no key yet (max still -inf) has nothing to scale
+                const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 m_run = m_new;
                 l_half *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        // O *= alpha in place, in the accumulation register
+                        float e = oacc[db][r];
+                        float tmp;
+                        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                                     : "+a"(e), "=&v"(tmp) : "v"(alpha));
+                        oacc[db][r] = e;
+                    }
             }
             // weights, their sum, and the PV operands (keys 16ks .. 16ks+15 of
             // the block are registers 8(ks&1) .. +7 of half ks>>1)
+            const float mref = m_run == kNegInf ? 0.f : m_run;
             frag_t pf[4];
             float psum = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + i] - m_run);
+                    const float p = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + i] - mref);
                     psum += p;
                     pf[ks][i] = (typename Mfma<T>::elem_t)p;
                 }

@@ -157,6 +157,151 @@ def record_traffic(run_dir: str, path: str | None = None) -> None:
     print(f"wrote {path}: {sorted(entries)} at source {sha}")
 
 
+def time_steps(torch, step, args, stream):
+    """The timing protocol: W untimed warm-up steps, the pause, K timed steps
+    between two synchronisations (wall clock and HIP events on the launch
+    stream), then a per-call spread outside the timed block."""
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.sleep > 0:
+        time.sleep(args.sleep)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (events)")
+    # per-call spread, after and outside the timed block: each call between
+    # its own pair of events on the launch stream
+    n_calls = min(50, max(10, args.steps // 4))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
+    spread = {"calls": n_calls, "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
+    return ms_per_step, kernel_ms, spread
+
+
+def roofline(flops, compulsory_bytes, kernel_ms):
+    """The bound: HBM when the flops per compulsory byte fall below the
+    machine balance (2516.6 TFLOP/s / 8 TB/s = 315 flop/B; the batched
+    short-K GEMM (228, its fp16 C writes) and the skinny GEMM (63) are),
+    else the matrix cores.  achieved = algorithmic work per launch over the
+    average launch duration."""
+    if flops / compulsory_bytes < PEAK_MFMA_F16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        achieved = compulsory_bytes / (kernel_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None}
+
+
+def gemm_setup(torch, pkg, inputs, args, dev):
+    """GEMM workload: rotating (A, B, C) sets resident in HBM, the step, the
+    config and the oracle baseline."""
+    w = inputs.WORKLOADS[args.workload]
+    R = w.rotating
+    log(f"workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
+        f"out={'fp32' if w.out_fp32 else w.dtype} rotating={R}")
+    As, Bs, Cs = [], [], []
+    A0 = B0 = None
+    nt = args.b_layout == "nt"
+    for j in range(R):
+        A = w.make_a(j) if (w.rotate_a or j == 0) else None
+        B = w.make_b(j)
+        if j == 0:
+            A0, B0 = A, B
+        As.append(A.to(dev) if A is not None else As[0])
+        Bd = B.to(dev)
+        Bs.append(Bd.transpose(-1, -2).contiguous() if nt else Bd)
+        out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
+        Cs.append(torch.empty(w.c_shape(), dtype=out_t, device=dev))
+    stream = torch.cuda.current_stream()
+    gemm = pkg.gemm_ex_bt if nt else pkg.gemm_ex
+
+    def step(i):
+        j = i % R
+        gemm(As[j], Bs[j], Cs[j], dtype=w.dtype, out_fp32=w.out_fp32, variant=args.variant, stream=stream)
+
+    variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.K if nt else w.N,
+                                                    w.out_fp32, bt=nt)
+    names = {v: k for k, v in pkg.variants().items()}
+    kernel = names.get(variant_id, str(variant_id))
+    metric = (METRIC if w.name == "f16_4096" and not nt else
+              f"{w.name}{' with B given transposed (N x K)' if nt else ''} TFLOPS (1 MI355X)")
+    config = {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+              "in": w.dtype, "out": "fp32" if w.out_fp32 else w.dtype, "accumulate": "fp32",
+              "rotating_buffers": R, "kernel": kernel, "b_layout": "N x K (transposed)" if nt else "K x N"}
+    return (w, step, stream, metric, config, kernel, lambda: cpu_baseline(w, A0, B0))
+
+
+def attention_cpu_baseline(w, q, k, v, budget_s: float = 15.0, min_s: float = 10.0):
+    """Time the oracle on the first R query rows of head 0 (all keys), R grown
+    until one call takes at least min_s seconds (or covers the head)."""
+    import numpy as np
+    import oracle
+    from barrier_pipelined_tiled_amd import inputs
+    qb, kb, vb = inputs.bits(q[0]), inputs.bits(k[0]), inputs.bits(v[0])
+    rows = 16
+    while True:
+        idx = (np.zeros(rows, dtype=np.int64), np.arange(rows, dtype=np.int64))
+        t0 = time.perf_counter()
+        oracle.attention(qb[None], kb[None], vb[None], w.scale, w.dtype, rows=idx)
+        t = time.perf_counter() - t0
+        if t >= min_s or rows == w.Sq:
+            break
+        rows = int(max(rows + 1, min(w.Sq, rows * budget_s / max(t, 1e-3))))
+        log(f"cpu_baseline: attention oracle on {rows} query rows ...")
+    flops = 4.0 * rows * w.Skv * w.D
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"query rows 0..{rows - 1} of head 0 against its {w.Skv} keys, D = {w.D}, "
+                  f"{w.dtype}, fp64, {t:.1f} s",
+    }
+
+
+def attention_setup(torch, pkg, inputs, args, dev):
+    w = inputs.ATTENTION[args.workload]
+    R = w.rotating
+    log(f"workload {w.name}: BH={w.BH} Sq={w.Sq} Skv={w.Skv} D={w.D} {w.dtype} rotating={R}")
+    sets = []
+    q0 = k0 = v0 = None
+    for j in range(R):
+        q, k, v = w.make_q(j), w.make_k(j), w.make_v(j)
+        if j == 0:
+            q0, k0, v0 = q, k, v
+        out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
+        sets.append((q.to(dev), k.to(dev), v.to(dev), torch.empty(q.shape, dtype=out_t, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v, o = sets[i % R]
+        pkg.attention_fwd(q, k, v, o, scale=w.scale, dtype=w.dtype, out_fp32=w.out_fp32, stream=stream)
+
+    kernel = f"attention_fwd_d{w.D}"
+    metric = f"{w.name} TFLOPS (1 MI355X): fused attention forward, 4 * BH * Sq * Skv * D flops"
+    config = {"workload": w.name, "batch_heads": w.BH, "seq_q": w.Sq, "seq_kv": w.Skv, "head_dim": w.D,
+              "in": w.dtype, "out": "fp32" if w.out_fp32 else w.dtype, "accumulate": "fp32",
+              "scale": w.scale, "rotating_buffers": R, "kernel": kernel}
+    return (w, step, stream, metric, config, kernel, lambda: attention_cpu_baseline(w, q0, k0, v0))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,13 +309,14 @@ def main():
     # again, which a 200-call block (26 ms at 4096^3) would mostly measure
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="f16_4096")
-    ap.add_argument("--variant", type=int, default=0, help="0 = automatic choice")
+    ap.add_argument("--workload", default="f16_4096",
+                    help="a GEMM workload (f16_4096, ...) or an attention one (attn_f16_...)")
+    ap.add_argument("--variant", type=int, default=0, help="GEMM variant, 0 = automatic choice")
     ap.add_argument("--sleep", type=float, default=5.0, help="pause before timing (s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
-                    help="kn: B is K x N (the workloads' layout); nt: the same B handed over "
-                         "transposed (N x K) through gemm_ex_bt")
+                    help="GEMM only.  kn: B is K x N (the workloads' layout); nt: the same B handed "
+                         "over transposed (N x K) through gemm_ex_bt")
     ap.add_argument("--record-traffic", metavar="RUN_DIR",
                     help="write profiles/traffic.json from the counter runs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -188,97 +334,29 @@ def main():
     import barrier_pipelined_tiled_amd as pkg
     from barrier_pipelined_tiled_amd import inputs
 
-    w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     pkg.lib()
-    R = w.rotating
-    log(f"workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
-        f"out={'fp32' if w.out_fp32 else w.dtype} rotating={R}")
-
-    As, Bs, Cs = [], [], []
-    A0 = B0 = None
-    for j in range(R):
-        A = w.make_a(j) if (w.rotate_a or j == 0) else None
-        B = w.make_b(j)
-        if j == 0:
-            A0, B0 = A, B
-        As.append(A.to(dev) if A is not None else As[0])
-        Bd = B.to(dev)
-        Bs.append(Bd.transpose(-1, -2).contiguous() if args.b_layout == "nt" else Bd)
-        out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
-        Cs.append(torch.empty(w.c_shape(), dtype=out_t, device=dev))
+    if args.workload in inputs.ATTENTION:
+        setup = attention_setup
+    elif args.workload in inputs.WORKLOADS:
+        setup = gemm_setup
+    else:
+        print(f"unknown workload {args.workload}; GEMM: {sorted(inputs.WORKLOADS)}, "
+              f"attention: {sorted(inputs.ATTENTION)}", file=sys.stderr)
+        sys.exit(2)
+    w, step, stream, metric, config, kernel, baseline = setup(torch, pkg, inputs, args, dev)
     torch.cuda.synchronize()
     log("inputs resident in HBM")
 
-    stream = torch.cuda.current_stream()
-
-    nt = args.b_layout == "nt"
-
-    def step(i):
-        j = i % R
-        gemm = pkg.gemm_ex_bt if nt else pkg.gemm_ex
-        gemm(As[j], Bs[j], Cs[j], dtype=w.dtype, out_fp32=w.out_fp32, variant=args.variant, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if args.sleep > 0:
-        time.sleep(args.sleep)
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (events)")
-
-    # per-call spread, after and outside the timed block: each call between
-    # its own pair of events on the launch stream
-    n_calls = min(50, max(10, args.steps // 4))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_call = sorted(a.elapsed_time(b) for a, b in evs)
-    pct = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
-    spread = {"calls": n_calls, "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
-
-    flops = w.flops
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    # the bound: HBM when the workload's flops per compulsory byte fall below
-    # the machine balance (2516.6 TFLOP/s / 8 TB/s = 315 flop/B); the batched
-    # short-K shape (228, its fp16 C writes) and the skinny shape (63) are
-    memory_bound = flops / w.compulsory_bytes < PEAK_MFMA_F16_TFLOPS / PEAK_HBM_GBS * 1e3
-    if memory_bound:
-        achieved = w.compulsory_bytes / (kernel_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
-    else:
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_F16_TFLOPS, "traffic": None}
-
-    variant_id = args.variant or pkg.select_variant(w.dtype, w.batch, w.M, w.N, w.K, w.K, w.K if nt else w.N,
-                                                    w.out_fp32, bt=nt)
-    names = {v: k for k, v in pkg.variants().items()}
-    roof["traffic"] = measured_traffic(w.name, names.get(variant_id, ""))
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, A0, B0)
+    ms_per_step, kernel_ms, spread = time_steps(torch, step, args, stream)
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    roof = roofline(w.flops, w.compulsory_bytes, kernel_ms)
+    roof["traffic"] = measured_traffic(w.name, kernel)
+    config["pct_of_dense_peak"] = 100.0 * value / PEAK_MFMA_F16_TFLOPS
+    cpu = None if args.no_cpu_baseline else baseline()
 
     out = {
-        "metric": (METRIC if w.name == "f16_4096" and not nt else
-                   f"{w.name}{' with B given transposed (N x K)' if nt else ''} TFLOPS (1 MI355X)"),
+        "metric": metric,
         "value": value,
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -290,11 +368,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if w.dtype == "f16" else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
-                   "in": w.dtype, "out": "fp32" if w.out_fp32 else w.dtype, "accumulate": "fp32",
-                   "rotating_buffers": R, "kernel": names.get(variant_id, str(variant_id)),
-                   "b_layout": "N x K (transposed)" if nt else "K x N",
-                   "pct_of_dense_peak": 100.0 * value / PEAK_MFMA_F16_TFLOPS},
+        "config": config,
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_call": spread,

@@ -192,3 +192,45 @@ def test_bt_layout_entry_point(L):
     # odd K and odd leading dimensions: the guarded kernel
     assert pkg.select_variant("f16", 1, 300, 201, 250, 250, 250, bt=True) == v["generic_bt_64x64x16"]
 
+
+
+def _attn(L, dtype=0, BH=2, Sq=128, Skv=64, D=256, Q=FAKE, ldq=256, sQ=0, K=FAKE, ldk=256, sK=0,
+          V=FAKE, ldv=256, sV=0, O=FAKE, ldo=256, sO=0, scale=0.0625, out_fp32=0):
+    return L.attention_fwd(dtype, BH, Sq, Skv, D, Q, ldq, sQ, K, ldk, sK, V, ldv, sV, O, ldo, sO,
+                           scale, out_fp32, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), pkg.BPT_ERR_INVALID_ARG),
+    (dict(out_fp32=3), pkg.BPT_ERR_INVALID_ARG),
+    (dict(BH=-1), pkg.BPT_ERR_INVALID_ARG),
+    (dict(Sq=-1), pkg.BPT_ERR_INVALID_ARG),
+    (dict(Skv=-1), pkg.BPT_ERR_INVALID_ARG),
+    (dict(D=0), pkg.BPT_ERR_INVALID_ARG),
+    (dict(ldq=128), pkg.BPT_ERR_INVALID_ARG),
+    (dict(ldk=255), pkg.BPT_ERR_INVALID_ARG),
+    (dict(ldv=8), pkg.BPT_ERR_INVALID_ARG),
+    (dict(ldo=200), pkg.BPT_ERR_INVALID_ARG),
+    (dict(sV=-8), pkg.BPT_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pkg.BPT_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), pkg.BPT_ERR_INVALID_ARG),
+    (dict(Q=0), pkg.BPT_ERR_INVALID_ARG),
+    (dict(O=0), pkg.BPT_ERR_INVALID_ARG),
+    (dict(K=0), pkg.BPT_ERR_INVALID_ARG),
+    (dict(V=0), pkg.BPT_ERR_INVALID_ARG),
+    (dict(D=64, ldq=64, ldk=64, ldv=64, ldo=64), pkg.BPT_ERR_UNSUPPORTED),     # head_dim not built
+    (dict(D=96, ldq=96, ldk=96, ldv=96, ldo=96), pkg.BPT_ERR_UNSUPPORTED),
+    (dict(Q=FAKE + 8), pkg.BPT_ERR_UNSUPPORTED),                              # 8-byte aligned base
+    (dict(ldk=260), pkg.BPT_ERR_UNSUPPORTED),                                 # row not 16-byte granular
+    (dict(sO=12), pkg.BPT_ERR_UNSUPPORTED),
+    (dict(Skv=1 << 22, ldk=256), pkg.BPT_ERR_UNSUPPORTED),                     # head's K extent >= 2^31 bytes
+])
+def test_attention_rejections(L, kw, status):
+    assert _attn(L, **kw) == status, kw
+    assert L.bpt_last_error().decode() != ""
+
+
+def test_attention_empty_calls_are_noops(L):
+    # nothing to compute: OK, no launch, NULL pointers allowed
+    assert _attn(L, BH=0, Q=0, K=0, V=0, O=0) == pkg.BPT_OK
+    assert _attn(L, Sq=0, Q=0, K=0, V=0, O=0) == pkg.BPT_OK
