@@ -113,7 +113,12 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
         const uint32_t vq = (uint32_t)(((wave * 32 + (lane & 31)) * a.ldq + 8 * h) * 2);
 #pragma unroll
         for (int t = 0; t < TS; ++t)
-            qf[t] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * 32, 0, 0));
+            qf[t] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rq, vq + t * 32, 0, 0));        // Let Q land here, with a wait the compiler sees: otherwise its wait
+        // counting carries the Q loads into the key loop as pending and puts
+        // vmcnt waits before their first uses there, which at run time also
+        // wait for the K/V copies just issued (LDS-DMA copies count in vmcnt
+        // but are invisible to the compiler).
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     float16_t oacc[DB];

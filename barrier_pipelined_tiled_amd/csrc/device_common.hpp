@@ -34,6 +34,20 @@ __device__ inline int4_t make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
+// s_waitcnt immediate for "vmcnt(0)" alone (expcnt and lgkmcnt at their
+// maxima, i.e. not waited for), for __builtin_amdgcn_s_waitcnt, which the
+// compiler's own wait insertion takes into account (an inline-asm wait is
+// opaque to it).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (loads and LDS-DMA copies complete in issue order).
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // 32-bit LDS address of a pointer into LDS.
 __device__ inline uint32_t lds_addr(const BPT_LDS void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);

@@ -42,12 +42,6 @@ struct SkinnyArgs {
     float* partial;         // splits > 1: [block][split][64][BN] fp32
 };
 
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 template <typename T, int WAVES, int KC, int SB, int SA, int NB, typename OutT>
 struct SkinnyGemm {
     static_assert(KC == 32 || KC == 64, "A swizzles exist for 64- and 128-byte rows");
