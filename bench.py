@@ -249,21 +249,24 @@ def gemm_setup(torch, pkg, inputs, args, dev):
 
 
 def attention_cpu_baseline(w, q, k, v, budget_s: float = 15.0, min_s: float = 10.0):
-    """Time the oracle on the first R query rows of head 0 (all keys), R grown
-    until one call takes at least min_s seconds (or covers the head)."""
+    """Time the oracle on the first R query rows (head by head, each against
+    all keys of its head), R grown until one call takes at least min_s
+    seconds (or covers every row)."""
     import numpy as np
     import oracle
     from barrier_pipelined_tiled_amd import inputs
-    qb, kb, vb = inputs.bits(q[0]), inputs.bits(k[0]), inputs.bits(v[0])
+    qb, kb, vb = inputs.bits(q), inputs.bits(k), inputs.bits(v)
+    total = w.BH * w.Sq
     rows = 16
     while True:
-        idx = (np.zeros(rows, dtype=np.int64), np.arange(rows, dtype=np.int64))
+        t_idx = np.arange(rows, dtype=np.int64)
+        idx = (t_idx // w.Sq, t_idx % w.Sq)
         t0 = time.perf_counter()
-        oracle.attention(qb[None], kb[None], vb[None], w.scale, w.dtype, rows=idx)
+        oracle.attention(qb, kb, vb, w.scale, w.dtype, rows=idx)
         t = time.perf_counter() - t0
-        if t >= min_s or rows == w.Sq:
+        if t >= min_s or rows == total:
             break
-        rows = int(max(rows + 1, min(w.Sq, rows * budget_s / max(t, 1e-3))))
+        rows = int(max(rows + 1, min(total, rows * budget_s / max(t, 1e-3))))
         log(f"cpu_baseline: attention oracle on {rows} query rows ...")
     flops = 4.0 * rows * w.Skv * w.D
     return {
@@ -271,8 +274,8 @@ def attention_cpu_baseline(w, q, k, v, budget_s: float = 15.0, min_s: float = 10
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"query rows 0..{rows - 1} of head 0 against its {w.Skv} keys, D = {w.D}, "
-                  f"{w.dtype}, fp64, {t:.1f} s",
+        "sample": f"the first {rows} query rows (heads 0..{(rows - 1) // w.Sq}), each against the "
+                  f"{w.Skv} keys of its head, D = {w.D}, {w.dtype}, fp64, {t:.1f} s",
     }
 
 
