@@ -602,10 +602,14 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t stream) {
     a.c2 = (float)((double)c.scale * 1.4426950408889634);     // scale * log2(e)
     a.q_tiles = (int)((c.Sq + 127) / 128);
     const dim3 grid((unsigned)(a.q_tiles * c.BH));
-    if (c.D == 256)
-        hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 256, OutT>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 128, OutT>), grid, dim3(256), 0, stream, a);
+    const bool pos = c.scale >= 0.f;
+    if (c.D == 256) {
+        if (pos) hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 256, OutT, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 256, OutT, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (pos) hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 128, OutT, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((bpt::attention_fwd_kernel<T, 128, OutT, false>), grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

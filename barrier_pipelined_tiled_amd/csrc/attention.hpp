@@ -77,7 +77,9 @@ struct AttnFwd {
 // GEMM's B swizzle (swz_b) already spreads the rows.
 __device__ inline int attn_swz_k(int row) { return row & 15; }
 
-template <typename T, int D, typename OutT>
+// POS: scale >= 0 (the row maximum of the logits is the maximum of the raw
+// products; for a negative scale it is the minimum).
+template <typename T, int D, typename OutT, bool POS>
 __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
     typedef AttnFwd<T, D> G;
     typedef typename Mfma<T>::frag_t frag_t;
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                             // half of the wave
     const float kNegInf = -__builtin_inff();
+    const float kFar = POS ? kNegInf : __builtin_inff(); // a raw product no row max can pick
 
     // XCD-aware order: a run of consecutive (head, query tile) pairs -- the
     // tiles of one head, sharing its K and V -- stays on one XCD's L2
@@ -189,22 +192,22 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                     frag_t kf = *(BPT_LDS frag_t*)(kt + rdK[t & 7] + (t >> 3) * 256 + kb * 32 * D * 2);
                     s[kb] = Mfma<T>::mma32(kf, qf[t], s[kb]);
                 }
-            // logits in base 2; key of register r of half kb: 64j + 32kb +
-            // 8(r/4) + 4h + r%4
-            float mloc = kNegInf;
+            // the row maximum of the logits in base 2, from the raw products
+            // (the scale is monotone; keys >= Skv excluded when MASK); register
+            // r of half kb holds key 64j + 32kb + 8(r/4) + 4h + r%4
+            auto masked = [&](int kb, int r) __attribute__((always_inline)) {
+                return MASK && j * BN + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) >= Skv;
+            };
+            float mraw = kFar;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float x = s[kb][r] * a.c2;
-                    if constexpr (MASK) {
-                        const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= Skv) x = -__builtin_inff();
-                    }
-                    s[kb][r] = x;
-                    mloc = __builtin_fmaxf(mloc, x);
+                    const float x = masked(kb, r) ? kFar : s[kb][r];
+                    mraw = POS ? __builtin_fmaxf(mraw, x) : __builtin_fminf(mraw, x);
                 }
-            mloc = __builtin_fmaxf(mloc, __shfl_xor(mloc, 32));
+            mraw = POS ? __builtin_fmaxf(mraw, __shfl_xor(mraw, 32)) : __builtin_fminf(mraw, __shfl_xor(mraw, 32));
+            const float mloc = mraw * a.c2;
             // raise the running max only when some row would otherwise see a
             // weight above 2^8
             if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.0f) != 0) {
@@ -225,20 +228,26 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                         oacc[db][r] = e;
                     }
             }
-            // weights, their sum, and the PV operands (keys 16ks .. 16ks+15 of
-            // the block are registers 8(ks&1) .. +7 of half ks>>1)
-            const float mref = m_run == kNegInf ? 0.f : m_run;
+            // weights p = 2^(s c2 - m) (one FMA into the exponent), rounded to
+            // the input type for the PV operands (keys 16ks .. 16ks+15 of the
+            // block are registers 8(ks&1) .. +7 of half ks>>1); the row sum
+            // adds the rounded weights, the values the PV product uses
+            const float nmref = m_run == kNegInf ? 0.f : -m_run;
             frag_t pf[4];
-            float psum = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + i] - mref);
-                    psum += p;
-                    pf[ks][i] = (typename Mfma<T>::elem_t)p;
+                    const int kb = ks >> 1, r = 8 * (ks & 1) + i;
+                    const float e2 = masked(kb, r) ? kNegInf : __builtin_fmaf(s[kb][r], a.c2, nmref);
+                    pf[ks][i] = (typename Mfma<T>::elem_t)__builtin_amdgcn_exp2f(e2);
                 }
-            l_half += psum;
+            float psum = l_half;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) psum = Mfma<T>::dot2(pf[ks][2 * i], pf[ks][2 * i + 1], psum);
+            l_half = psum;
             // O^T += V^T P^T
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)

@@ -102,6 +102,11 @@ struct Mfma<_Float16> {
     __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    // acc + x + y in one v_dot2 (the pair dotted with (1, 1), fp32 sum)
+    __device__ static inline float dot2(elem_t x, elem_t y, float acc) {
+        typedef _Float16 pair_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(pair_t{x, y}, pair_t{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+    }
 };
 
 template <>
@@ -110,6 +115,10 @@ struct Mfma<__bf16> {
     typedef bf16x8_t frag_t;
     __device__ static inline float16_t mma32(frag_t a, frag_t b, float16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline float dot2(elem_t x, elem_t y, float acc) {
+        typedef __bf16 pair_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(pair_t{x, y}, pair_t{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
     }
 };
 

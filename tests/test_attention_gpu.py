@@ -76,6 +76,30 @@ def test_parity_sharp_logits(scale):
     check_random(q, k, v, scale, "f16", True)
 
 
+@pytest.mark.parametrize("D,Skv", [(256, 300), (128, 1024)])
+def test_parity_negative_scale(D, Skv):
+    """A negative scale turns the row maximum of the logits into the minimum
+    of the raw products (its own code path); ragged Skv masks the tail."""
+    say(f"attention negative scale D={D} Skv={Skv}")
+    q = inputs.uniform((2, 150, D), 2051, lo=-0.5, hi=0.5)
+    k = inputs.uniform((2, Skv, D), 2052, lo=-0.5, hi=0.5)
+    v = inputs.uniform((2, Skv, D), 2053)
+    check_random(q, k, v, -0.75, "f16", True)
+
+
+def test_zero_scale_exact():
+    """scale 0: every logit is 0 whatever Q and K are, so O is the mean of
+    the values, exactly for integers over a power-of-two key count."""
+    say("attention zero scale")
+    BH, Sq, Skv, D = 2, 70, 512, 256
+    q = inputs.uniform((BH, Sq, D), 2061)
+    k = inputs.uniform((BH, Skv, D), 2062)
+    v = inputs.small_integers((BH, Skv, D), 2063, -3, 3)
+    ref = oracle.attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), 0.0)
+    got = run_attention(q, k, v, 0.0, "f16", True)
+    assert np.array_equal(got.numpy(), ref)
+
+
 def test_rising_maximum_across_blocks():
     """Keys whose logits grow block by block (key j scaled by j/Skv): every
     block raises each row's maximum, many times over 2^8."""
