@@ -292,6 +292,8 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                 out4_t v;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) v[q] = cvt_out<OutT>(oacc[db][4 * r4 + q] * inv);
+                // plain stores: each lane writes 8-byte pieces of its row, which
+                // the L2 merges (non-temporal stores measured 2% slower here)
                 *(out4_t*)(orow + 32 * db + 8 * r4 + 4 * h) = v;
             }
     }
