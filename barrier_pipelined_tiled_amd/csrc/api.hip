@@ -15,6 +15,7 @@
 
 #include "../../include/bpt_gemm.h"
 #include "attention.hpp"
+#include "gemm_apair.hpp"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
@@ -51,7 +52,8 @@ enum Variant {
     V_BT_128_K32_S4 = 11,   // 128x128 tile, BK 32, 4 stages
     V_BT_GENERIC = 12,      // guarded 64x64, any shape / alignment
     V_BT_256_K64_S2 = 13,   // 256x256 tile, BK 64 (128-byte rows of A and Bt), 2 stages
-    V_COUNT = 13
+    V_PIPE_256_K32_S4_AP = 14,  // 256x256 tile, BK 32, 4 B stages, A copied in K-tile pairs (whole lines)
+    V_COUNT = 14
 };
 
 bool is_bt_variant(int v) { return v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2; }
@@ -71,11 +73,12 @@ const char* const kVariantNames[] = {
     "pipelined_bt_128x128x32_s4",
     "generic_bt_64x64x16",
     "pipelined_bt_256x256x64_s2",
+    "pipelined_256x256x32_s4_apair",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -240,9 +243,19 @@ int choose_bt(const Call& c) {
 
 // the pipelined variant for a call one of them accepts in place (or for its
 // repacked form); V_GENERIC when none does
+// The A-pair variant reads A in 64-wide K pairs: K a multiple of 64 with at
+// least 6 K-tiles (the 4-stage B ring plus a pair), no K tail; otherwise the
+// requirements of the 32-wide 4-stage kernel.
+bool apair_ok(const Call& c) {
+    return c.K % 64 == 0 && c.K >= 192 && pipelined_ok(c, 32, 4, false);
+}
+
 int choose_pipelined(const Call& c) {
     const long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     const bool big = tiles256 >= 128;
+    // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
+    // 1393 -> 1417 against the 32-wide 4-stage kernel on the same box
+    if (big && apair_ok(c)) return V_PIPE_256_K32_S4_AP;
     if (big && pipelined_ok(c, 32, 4, variant_tail(V_PIPE_256_K32_S4))) return V_PIPE_256_K32_S4;
     if (pipelined_ok(c, 32, 4, variant_tail(V_PIPE_128_K32_S4))) return V_PIPE_128_K32_S4;
     if (big && pipelined_ok(c, 64, 2, variant_tail(V_PIPE_256_K64_S2))) return V_PIPE_256_K64_S2;
@@ -358,6 +371,30 @@ hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
         hipLaunchKernelGGL((bpt::gemm_pipelined_kernel<T, BM, BN, BK, STAGES, 2, 2, OutT, BT>),
                            dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t launch_apair(const Call& c, hipStream_t stream) {
+    bpt::GemmArgs a;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_m = (int)((c.M + 255) / 256);
+    a.tiles_n = (int)((c.N + 255) / 256);
+    a.group_m = 4;
+    const long long ob = (long long)sizeof(OutT);
+    a.c_vec = aligned16(c.C) && (c.ldc * ob) % 16 == 0 && (c.sC * ob) % 16 == 0;
+    a.nb = (int)(c.nb > 0 ? c.nb : c.N);
+    const long long tiles = (long long)a.tiles_m * a.tiles_n;
+    for (long long b0 = 0; b0 < c.batch; b0 += 65535) {
+        long long nb = c.batch - b0 < 65535 ? c.batch - b0 : 65535;
+        a.A = static_cast<const T*>(c.A) + b0 * c.sA;
+        a.B = static_cast<const T*>(c.B) + b0 * c.sB;
+        a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
+        hipLaunchKernelGGL((bpt::gemm_apair_kernel<T, OutT>), dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0,
+                           stream, a);
     }
     return hipGetLastError();
 }
@@ -515,6 +552,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_BT_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4, true>(c, stream);
         case V_BT_GENERIC: return launch_generic<T, OutT, true>(c, stream);
         case V_BT_256_K64_S2: return launch_pipelined<T, OutT, 256, 256, 64, 2, true>(c, stream);
+        case V_PIPE_256_K32_S4_AP: return launch_apair<T, OutT>(c, stream);
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -554,6 +592,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_SKINNY: return skinny_ok(c);
         case V_SKINNY_WIDE: return wide_splits(c) > 0;
         case V_REPACK: return repack_feasible(c);
+        case V_PIPE_256_K32_S4_AP: return apair_ok(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

@@ -167,6 +167,79 @@ struct PipelinedGemm {
     typedef typename Mfma<T>::frag_t frag_t;
 };
 
+// ---- a8: epilogue ------------------------------------------------------------
+// (shared by the pipelined kernels; G supplies the wave tile and staging
+// geometry)
+template <typename G, typename OutT>
+__device__ inline void pipelined_epilogue(const GemmArgs& args, const float16_t (&acc)[G::MB][G::NB],
+                                          BPT_LDS char* lds, int lane, int wave, int wm, int wn, int m0,
+                                          int n0, int batch) {
+    constexpr int MB = G::MB, NB = G::NB;
+    const int M = args.M, N = args.N;
+    // Result layout (B fragment as first MFMA operand): lane l, register r of
+    // block (mb, nb) holds row mb*32 + l%32, column nb*32 + 8*(r/4) +
+    // 4*(l/32) + r%4 of the wave tile.  Each wave stages its tile in LDS
+    // (row-major, padded rows) and then writes whole rows, 16 bytes a lane.
+    publish<0>();                          // every wave is done with the ring
+    OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
+    const int ldc = args.ldc;
+    const int row0 = m0 + wm * G::TM;      // first C row / column of this wave
+    const int col0 = n0 + wn * G::TN;
+    const bool vec = args.c_vec && (row0 + G::TM <= M) && (col0 + G::TN <= N);
+    BPT_LDS char* stage_w = lds + wave * (G::EPI_ROWS * G::EPI_PITCH);
+    constexpr int OB = (int)sizeof(OutT);
+    constexpr int CH_PER_ROW = G::TN * OB / 16;            // 16-byte chunks per wave-tile row
+    constexpr int ROWS_PER_IT = 64 / CH_PER_ROW;
+    typedef OutT out4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int pass = 0; pass < G::EPI_PASSES; ++pass) {
+        constexpr int MBP = MB / G::EPI_PASSES;
+#pragma unroll
+        for (int mbp = 0; mbp < MBP; ++mbp) {
+            const int mb = pass * MBP + mbp;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    out4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = cvt_out<OutT>(acc[mb][nb][4 * g + e]);
+                    const int r = mbp * 32 + (lane % 32);
+                    const int c = nb * 32 + 8 * g + 4 * (lane / 32);
+                    *(BPT_LDS out4_t*)(stage_w + r * G::EPI_PITCH + c * OB) = v;
+                }
+        }
+        wave_lds_handoff();                        // rows written by other lanes are read below
+#pragma unroll
+        for (int it = 0; it < G::EPI_ROWS / ROWS_PER_IT; ++it) {
+            const int r = it * ROWS_PER_IT + lane / CH_PER_ROW;
+            const int ch = lane % CH_PER_ROW;
+            int4_t v = *(BPT_LDS int4_t*)(stage_w + r * G::EPI_PITCH + ch * 16);
+            const int grow = row0 + pass * G::EPI_ROWS + r;
+            const int gcol = col0 + ch * (16 / OB);
+            OutT* dst = Cb + (long long)grow * ldc + gcol;
+            // a 16-byte chunk is wholly inside C or outside when N % 8 == 0;
+            // only repacked calls (N % 8 != 0) have chunks that straddle N
+            if (vec || (grow < M && gcol < N)) {
+                if (args.c_vec && gcol + 16 / OB <= N) {
+                    // non-temporal: C is written once and never read back
+                    // here; stores that do not allocate in the L2 measured
+                    // 8% faster on the batched shape (2 GiB of C per call),
+                    // 1.5-2% on 4096^3 and the long-K shape
+                    __builtin_nontemporal_store(v, (int4_t*)dst);
+                } else {
+                    OutT vals[16 / OB];
+                    __builtin_memcpy(vals, &v, 16);
+#pragma unroll 1
+                    for (int e = 0; e < 16 / OB; ++e)
+                        if (gcol + e < N) dst[e] = vals[e];
+                }
+            }
+        }
+        wave_lds_handoff();                        // the next pass overwrites what was just read
+    }
+}
+
 template <typename T, int BM, int BN, int BK, int STAGES, int WM, int WN, typename OutT, bool BT = false>
 __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     typedef PipelinedGemm<T, BM, BN, BK, STAGES, WM, WN, OutT, BT> G;
@@ -452,68 +525,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipelined_kernel(GemmArgs args) {
     }
 
     // ---- a8: epilogue ---------------------------------------------------------
-    // Result layout (B fragment as first MFMA operand): lane l, register r of
-    // block (mb, nb) holds row mb*32 + l%32, column nb*32 + 8*(r/4) +
-    // 4*(l/32) + r%4 of the wave tile.  Each wave stages its tile in LDS
-    // (row-major, padded rows) and then writes whole rows, 16 bytes a lane.
-    publish<0>();                          // every wave is done with the ring
-    OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
-    const int ldc = args.ldc;
-    const int row0 = m0 + wm * G::TM;      // first C row / column of this wave
-    const int col0 = n0 + wn * G::TN;
-    const bool vec = args.c_vec && (row0 + G::TM <= M) && (col0 + G::TN <= N);
-    BPT_LDS char* stage_w = lds + wave * (G::EPI_ROWS * G::EPI_PITCH);
-    constexpr int OB = (int)sizeof(OutT);
-    constexpr int CH_PER_ROW = G::TN * OB / 16;            // 16-byte chunks per wave-tile row
-    constexpr int ROWS_PER_IT = 64 / CH_PER_ROW;
-    typedef OutT out4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int pass = 0; pass < G::EPI_PASSES; ++pass) {
-        constexpr int MBP = MB / G::EPI_PASSES;
-#pragma unroll
-        for (int mbp = 0; mbp < MBP; ++mbp) {
-            const int mb = pass * MBP + mbp;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    out4_t v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = cvt_out<OutT>(acc[mb][nb][4 * g + e]);
-                    const int r = mbp * 32 + (lane % 32);
-                    const int c = nb * 32 + 8 * g + 4 * (lane / 32);
-                    *(BPT_LDS out4_t*)(stage_w + r * G::EPI_PITCH + c * OB) = v;
-                }
-        }
-        wave_lds_handoff();                        // rows written by other lanes are read below
-#pragma unroll
-        for (int it = 0; it < G::EPI_ROWS / ROWS_PER_IT; ++it) {
-            const int r = it * ROWS_PER_IT + lane / CH_PER_ROW;
-            const int ch = lane % CH_PER_ROW;
-            int4_t v = *(BPT_LDS int4_t*)(stage_w + r * G::EPI_PITCH + ch * 16);
-            const int grow = row0 + pass * G::EPI_ROWS + r;
-            const int gcol = col0 + ch * (16 / OB);
-            OutT* dst = Cb + (long long)grow * ldc + gcol;
-            // a 16-byte chunk is wholly inside C or outside when N % 8 == 0;
-            // only repacked calls (N % 8 != 0) have chunks that straddle N
-            if (vec || (grow < M && gcol < N)) {
-                if (args.c_vec && gcol + 16 / OB <= N) {
-                    // non-temporal: C is written once and never read back
-                    // here; stores that do not allocate in the L2 measured
-                    // 8% faster on the batched shape (2 GiB of C per call),
-                    // 1.5-2% on 4096^3 and the long-K shape
-                    __builtin_nontemporal_store(v, (int4_t*)dst);
-                } else {
-                    OutT vals[16 / OB];
-                    __builtin_memcpy(vals, &v, 16);
-#pragma unroll 1
-                    for (int e = 0; e < 16 / OB; ++e)
-                        if (gcol + e < N) dst[e] = vals[e];
-                }
-            }
-        }
-        wave_lds_handoff();                        // the next pass overwrites what was just read
-    }
+    pipelined_epilogue<G, OutT>(args, acc, lds, lane, wave, wm, wn, m0, n0, batch);
 }
 
 }  // namespace bpt

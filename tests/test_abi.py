@@ -106,6 +106,18 @@ def test_empty_shapes_are_noops(L):
     assert L.gemm_batched_f16(0, 16, 16, 16, 0, 16, 0, 0, 16, 0, 0, 16, 0, 0, None) == pkg.BPT_OK
 
 
+def test_apair_variant_requirements(L):
+    """The A-pair kernel reads A in 64-wide K pairs with a 4-stage B ring:
+    K must be a multiple of 64 and at least 192; no K tail."""
+    v = pkg.variants()["pipelined_256x256x32_s4_apair"]
+    for K in (64, 128, 96, 200, 4104):
+        st = L.gemm_ex(0, 1, 256, 256, K, FAKE, K, 0, FAKE, 256, 0, FAKE, 256, 0, 0, v, None)
+        assert st == pkg.BPT_ERR_UNSUPPORTED, K
+    # B given transposed is not its layout
+    st = L.gemm_ex_bt(0, 1, 256, 256, 256, FAKE, 256, 0, FAKE, 256, 0, FAKE, 256, 0, 0, v, None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+
+
 def test_forced_variant_that_cannot_take_the_call(L):
     v = pkg.variants()["pipelined_256x256x64_s2"]
     # K = 100 is not a multiple of the 64-wide K-tile
@@ -119,9 +131,14 @@ def test_forced_variant_that_cannot_take_the_call(L):
 def test_automatic_variant_choice():
     v = pkg.variants()
     big = v["pipelined_256x256x32_s4"]
-    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == big
-    assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == big
-    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == big
+    # K a multiple of 64 (and >= 192): A copied in K-tile pairs, whole lines
+    apair = v["pipelined_256x256x32_s4_apair"]
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == apair
+    assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == apair
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == apair
+    assert pkg.select_variant("f16", 1, 4096, 4096, 192, 192, 4096) == apair
+    # K = 160 (five 32-wide tiles): too short for the pair ring, the 4-stage kernel
+    assert pkg.select_variant("f16", 1, 4096, 4096, 160, 160, 4096) == big
     assert pkg.select_variant("f16", 1, 256, 256, 256, 256, 256) == v["pipelined_128x128x32_s4"]
     # K = 96: three 32-wide tiles (< 4 stages) and not a multiple of 64
     assert pkg.select_variant("f16", 1, 256, 256, 96, 96, 256) == v["generic_64x64x16"]

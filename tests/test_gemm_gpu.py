@@ -66,7 +66,8 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
             "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
-            "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk", "repack_pipelined"]
+            "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk", "repack_pipelined",
+            "pipelined_256x256x32_s4_apair"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
 # least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
 # aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
