@@ -10,18 +10,22 @@
 // V and the prefetch of the next K placed between the barrier's arrive and
 // its wait.  On gfx950 the same schedule is rebuilt as follows.
 //
-// * Workgroup: 4 waves, 128 query rows; wave w owns rows 32w .. 32w+31 and
-//   keeps its Q fragments in registers for the whole key loop.  Every
+// * Workgroup: WAVES waves of 32 query rows; wave w owns rows 32w .. 32w+31
+//   and keeps its Q fragments in registers for the whole key loop.  Every
 //   softmax statistic of a row lives in that row's two lanes (l and l+32),
 //   so no reduction crosses waves -- the pages' barrier for the shared
-//   softmax maximum has nothing to do here.
-// * K and V blocks of 64 keys are staged global->LDS by LDS-DMA in a ring of
-//   two stages.  Block j is published by a vmcnt wait plus one s_barrier;
-//   right after it the copies of block j+1 are issued into the other stage
-//   (the window), and the math of block j follows.
+//   softmax maximum has nothing to do here.  With 8 waves, two share each
+//   SIMD: while one runs its softmax on the vector unit, the other's matrix
+//   products keep the matrix core busy (a wave alone leaves it idle through
+//   its softmax).  That needs a wave to fit in 256 registers, which at head
+//   dimension 256 holds for 32-key blocks.
+// * K and V blocks of BN keys are staged global->LDS by LDS-DMA in a ring of
+//   STAGES stages.  Block j is published by a vmcnt wait plus one s_barrier;
+//   right after it the copies of block j+STAGES-1 are issued into the stage
+//   block j-1 left (the window), and the math of block j follows.
 // * S never goes through LDS.  S^T = K Q^T is formed with K as the MFMA's
-//   row operand, so lane l holds query row l%32 and 16 keys of each 32-key
-//   half-block.  Those are exactly the keys its half of the wave must supply
+//   row operand, so lane l holds query row l%32 and 16 keys of each 32 keys
+//   of a block.  Those are exactly the keys its half of the wave must supply
 //   to the PV product if the key order inside each 16-key step is permuted
 //   (keys 4h..4h+3 and 8+4h..8+4h+3 for half h), and V is read from LDS with
 //   the same permutation (transposing reads of rows 4h.. and 8+4h..).  So P
@@ -34,7 +38,7 @@
 //   it, in the accumulation registers (read, multiply, write back per
 //   value); written as a plain multiply, it makes the compiler keep a second
 //   copy of O in ordinary registers and refresh it on every key block.
-// * The last key block, when Skv is not a multiple of 64, is peeled from the
+// * The last key block, when Skv is not a multiple of BN, is peeled from the
 //   loop and masks keys >= Skv to -inf; K and V rows past Skv read as zero
 //   (the buffer range check).
 #pragma once
@@ -52,23 +56,31 @@ struct AttnArgs {
     int ldq, ldk, ldv, ldo;                 // row strides (elements)
     long long sQ, sK, sV, sO;               // per (batch x head) strides (elements)
     float c2;                               // scale * log2(e)
-    int q_tiles;                            // ceil(Sq / 128)
+    int q_tiles;                            // ceil(Sq / BM)
 };
 
-template <typename T, int D>
+// WAVES_ waves of 32 query rows each, key blocks of BN_ keys, a ring of
+// STAGES_ K+V stages
+template <typename T, int D, int WAVES_, int BN_, int STAGES_>
 struct AttnFwd {
     static_assert(D == 128 || D == 256, "head dimensions 128 and 256");
-    static constexpr int WAVES = 4, BM = 128, BN = 64;
+    static_assert(BN_ == 32 || BN_ == 64, "key blocks of 32 or 64");
+    static_assert(STAGES_ == 2 || STAGES_ == 4, "power-of-two rings");
+    static constexpr int WAVES = WAVES_, BM = 32 * WAVES_, BN = BN_, STAGES = STAGES_;
+    static constexpr int KB = BN / 32;                  // 32-key halves of a block
+    static constexpr int PVS = BN / 16;                 // 16-key steps of the PV product
     static constexpr int DC = D / 8;                    // 16-byte chunks per row
     static constexpr int ROWS_PER_KIB = 1024 / (D * 2); // rows one wave-wide copy covers
     static constexpr int TILE = BN * D * 2;             // one K or V block in LDS
     static constexpr int STAGE = 2 * TILE;
-    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int LDS_BYTES = STAGES * STAGE;
     static constexpr int COPIES = TILE / 1024 / WAVES;  // per wave per tile
     static constexpr int TS = D / 16;                   // k-steps of Q K^T
     static constexpr int DB = D / 32;                   // 32-wide d blocks of O
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-    static_assert(2 * COPIES < 64, "vmcnt");
+    static_assert(COPIES >= 1, "every wave copies");
+    static constexpr int VM_AHEAD = (STAGES - 2) * 2 * COPIES;   // younger copies a publish lets fly
+    static_assert(VM_AHEAD + 2 * COPIES < 64, "vmcnt");
 };
 
 // K rows are read 32 at a time at one 16-byte chunk (ds_read_b128 into the
@@ -79,9 +91,9 @@ __device__ inline int attn_swz_k(int row) { return row & 15; }
 
 // POS: scale >= 0 (the row maximum of the logits is the maximum of the raw
 // products; for a negative scale it is the minimum).
-template <typename T, int D, typename OutT, bool POS>
-__global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
-    typedef AttnFwd<T, D> G;
+template <typename T, int D, typename OutT, bool POS, int WAVES, int BN_, int STAGES>
+__global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a) {
+    typedef AttnFwd<T, D, WAVES, BN_, STAGES> G;
     typedef typename Mfma<T>::frag_t frag_t;
     constexpr int BN = G::BN, TS = G::TS, DB = G::DB;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
@@ -148,8 +160,9 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
         }
         const uint32_t ldsb = __builtin_amdgcn_readfirstlane(lds_addr(lds));
         const uint32_t kstepK = (uint32_t)(BN * a.ldk * 2), kstepV = (uint32_t)(BN * a.ldv * 2);
+        // block j into stage j % STAGES (blocks past the last read zeros)
         auto issue = [&](int j) __attribute__((always_inline)) {
-            const uint32_t st = ldsb + (j & 1) * G::STAGE + wave * G::COPIES * 1024;
+            const uint32_t st = ldsb + (j & (STAGES - 1)) * G::STAGE + wave * G::COPIES * 1024;
 #pragma unroll
             for (int i = 0; i < G::COPIES; ++i) dma16(rsK, st + i * 1024, voffK[i] + j * kstepK, 0);
 #pragma unroll
@@ -178,29 +191,29 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                                  16 * (xv ^ (sv & 3)) + 8 * (jj & 1));
 
         auto block = [&]<bool MASK>(int j) __attribute__((always_inline)) {
-            BPT_LDS char* kt = lds + (j & 1) * G::STAGE;
+            BPT_LDS char* kt = lds + (j & (STAGES - 1)) * G::STAGE;
             BPT_LDS char* vt = kt + G::TILE;
-            // S^T for keys 64j .. 64j+63 (two 32-key halves)
-            float16_t s[2];
+            // S^T for keys BN j .. BN j + BN-1 (KB 32-key halves)
+            float16_t s[G::KB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < G::KB; ++kb)
                 s[kb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < TS; ++t)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < G::KB; ++kb) {
                     frag_t kf = *(BPT_LDS frag_t*)(kt + rdK[t & 7] + (t >> 3) * 256 + kb * 32 * D * 2);
                     s[kb] = Mfma<T>::mma32(kf, qf[t], s[kb]);
                 }
             // the row maximum of the logits in base 2, from the raw products
             // (the scale is monotone; keys >= Skv excluded when MASK); register
-            // r of half kb holds key 64j + 32kb + 8(r/4) + 4h + r%4
+            // r of half kb holds key BN j + 32kb + 8(r/4) + 4h + r%4
             auto masked = [&](int kb, int r) __attribute__((always_inline)) {
                 return MASK && j * BN + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3) >= Skv;
             };
             float mraw = kFar;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float x = masked(kb, r) ? kFar : s[kb][r];
@@ -233,9 +246,9 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
             // block are registers 8(ks&1) .. +7 of half ks>>1); the row sum
             // adds the rounded weights, the values the PV product uses
             const float nmref = m_run == kNegInf ? 0.f : -m_run;
-            frag_t pf[4];
+            frag_t pf[G::PVS];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < G::PVS; ++ks)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int kb = ks >> 1, r = 8 * (ks & 1) + i;
@@ -244,13 +257,13 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                 }
             float psum = l_half;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < G::PVS; ++ks)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) psum = Mfma<T>::dot2(pf[ks][2 * i], pf[ks][2 * i + 1], psum);
             l_half = psum;
             // O^T += V^T P^T
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int ks = 0; ks < G::PVS; ++ks)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     BPT_LDS char* p = vt + rdV[db & 3] + (db >> 2) * 256 + ks * 16 * D * 2;
@@ -261,21 +274,33 @@ __global__ __launch_bounds__(256, 1) void attention_fwd_kernel(AttnArgs a) {
                 }
         };
 
-        issue(0);
+        // Ring of STAGES: blocks 0 .. STAGES-2 are copied ahead; step j
+        // publishes block j, then copies block j+STAGES-1 into the stage
+        // block j-1 left.  Copies are issued past the last block too (they
+        // read zeros), so every publish lets the same STAGES-2 younger
+        // blocks stay in flight.
+        // publish block j: this wave's copies of it landed (vmcnt), every
+        // wave's copies landed and every wave is done with block j-1
+        // (s_barrier)
+        auto publish = [&]() __attribute__((always_inline)) {
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(G::VM_AHEAD) : "memory");
+        };
+#pragma unroll
+        for (int b = 0; b < STAGES - 1; ++b) issue(b);
         const bool ragged = (Skv % BN) != 0;
         const int nfull = ragged ? nblk - 1 : nblk;
         int j = 0;
         for (; j < nfull; ++j) {
-            // publish block j: this wave's copies landed (vmcnt), every wave's
-            // copies landed and every wave is done with block j-1 (s_barrier)
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (j + 1 < nblk) issue(j + 1);
+            publish();
+            issue(j + STAGES - 1);
             block.template operator()<false>(j);
         }
         if (ragged) {
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            publish();
             block.template operator()<true>(j);
         }
+        // no copy may still be writing LDS when the workgroup ends
+        wait_vm<0>();
     }
 
     // ---- O = O / l, rows < Sq ------------------------------------------------

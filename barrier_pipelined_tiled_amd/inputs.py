@@ -217,4 +217,7 @@ ATTENTION = {
     # as that product's operands
     "attn_f16_64x4096x4096x256": AttentionWorkload("attn_f16_64x4096x4096x256", "f16", 64, 4096, 4096, 256,
                                                    False, {"lo": -0.5, "hi": 0.5}, base_seed=202, rotating=2),
+    # the same at head dimension 128
+    "attn_f16_64x4096x4096x128": AttentionWorkload("attn_f16_64x4096x4096x128", "f16", 64, 4096, 4096, 128,
+                                                   False, {"lo": -0.5, "hi": 0.5}, base_seed=203, rotating=2),
 }
