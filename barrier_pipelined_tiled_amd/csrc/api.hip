@@ -53,7 +53,8 @@ enum Variant {
     V_BT_GENERIC = 12,      // guarded 64x64, any shape / alignment
     V_BT_256_K64_S2 = 13,   // 256x256 tile, BK 64 (128-byte rows of A and Bt), 2 stages
     V_PIPE_256_K32_S4_AP = 14,  // 256x256 tile, BK 32, 4 B stages, A copied in K-tile pairs (whole lines)
-    V_COUNT = 14
+    V_SKINNY_RING = 15,     // 64x128 block, waves split the columns, one shared 4-stage ring, + split-sum kernel
+    V_COUNT = 15
 };
 
 bool is_bt_variant(int v) { return v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2; }
@@ -74,11 +75,12 @@ const char* const kVariantNames[] = {
     "generic_bt_64x64x16",
     "pipelined_bt_256x256x64_s2",
     "pipelined_256x256x32_s4_apair",
+    "skinny_64x128_ring_k32_s4_splitk",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -162,21 +164,34 @@ bool wide_split_fits(const Call& c, int S) {
     return c.K % per == 0 && c.K / per >= kSwStages;
 }
 
-// Splits for the wide kernel: the fewest that give one workgroup per CU
-// (256), else the most that K allows, within the workspace limit; 0 when
-// the kernel cannot take the call.
-int wide_splits(const Call& c) {
-    if (c.K <= 0 || !skinny_operands_ok(c) || !wide_split_fits(c, 1)) return 0;
+// the shared-ring skinny kernel: same blocks and workspace, 32-deep K
+// chunks, a 4-stage ring for the workgroup (48 KiB; 3, 6, 8 and 12 stages
+// and 64-deep chunks measured slower on 64 x 8192 x 8192); any whole number
+// of chunks per split
+constexpr int kSrChunk = 32, kSrStages = 4;
+
+bool ring_split_fits(const Call& c, int S) {
+    return c.K % ((long long)S * kSrChunk) == 0;
+}
+
+// Splits for the split-K skinny kernels: the fewest that give one
+// workgroup per CU (256), else the most that K allows, within the workspace
+// limit; 0 when the kernel cannot take the call.
+int skinny_splits(const Call& c, bool (*fits)(const Call&, int), long long target = 256) {
+    if (c.K <= 0 || !skinny_operands_ok(c) || !fits(c, 1)) return 0;
     const long long blocks = wide_blocks_per_launch(c);
     int best = 1;
     for (int S = 2; S <= 8; S *= 2) {
-        if (!wide_split_fits(c, S)) break;
+        if (!fits(c, S)) break;
         if (blocks * S * 64 * kSwBN * 4 > kWorkspaceMax) break;
-        if (blocks * best >= 256) break;
+        if (blocks * best >= target) break;
         best = S;
     }
     return best;
 }
+
+int wide_splits(const Call& c) { return skinny_splits(c, wide_split_fits); }
+int ring_splits(const Call& c) { return skinny_splits(c, ring_split_fits); }
 
 // One device workspace per (device, stream), grown on demand.  A grown-out
 // buffer is kept, not freed, until the process ends: a call on another host
@@ -338,11 +353,13 @@ bool variant_tail(int v) {
 int choose(const Call& c) {
     if (c.bt) return choose_bt(c);
     // few rows of A: stream B once with a skinny kernel when that yields at
-    // least half a workgroup per CU; the wide one reads B in 256-byte row
-    // pieces, which stream faster than the narrow one's 64-byte pieces
+    // least half a workgroup per CU; the 128-column ones read B in 256-byte
+    // row pieces, which stream faster than the narrow one's 64-byte pieces,
+    // and the shared-ring one of them streams fastest and takes any K that
+    // is a multiple of 32
     if (c.M <= 64) {
-        const int S = wide_splits(c);
-        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_WIDE;
+        const int S = ring_splits(c);
+        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
         if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
     }
     const int v = choose_pipelined(c);
@@ -429,9 +446,9 @@ void launch_split_sum(const bpt::SkinnySumArgs& a, int S, hipStream_t stream) {
     else hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 8, OutT>), grid, dim3(256), 0, stream, a);
 }
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool RING = false>
 hipError_t launch_skinny_wide(const Call& c, hipStream_t stream) {
-    int S = wide_splits(c);
+    int S = RING ? ring_splits(c) : wide_splits(c);
     float* ws = nullptr;
     if (S > 1) {
         ws = stream_workspace(wide_blocks_per_launch(c) * S * 64 * kSwBN * 4, stream);
@@ -457,9 +474,13 @@ hipError_t launch_skinny_wide(const Call& c, hipStream_t stream) {
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;
         a.B = static_cast<const T*>(c.B) + b0 * c.sB;
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
-        hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSwWaves, kSwChunk, kSwStages, kSwSlots, 4, OutT>),
-                           dim3((unsigned)(a.tiles_n * S), (unsigned)tm, (unsigned)nb), dim3(kSwWaves * 64), 0,
-                           stream, a);
+        const dim3 grid((unsigned)(a.tiles_n * S), (unsigned)tm, (unsigned)nb);
+        if constexpr (RING)
+            hipLaunchKernelGGL((bpt::gemm_skinny_ring_kernel<T, kSrChunk, kSrStages, OutT>), grid, dim3(256), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((bpt::gemm_skinny_kernel<T, kSwWaves, kSwChunk, kSwStages, kSwSlots, 4, OutT>), grid,
+                               dim3(kSwWaves * 64), 0, stream, a);
         if (S > 1) {
             r.C = a.C;
             r.blocks = a.tiles_n * tm * nb;
@@ -547,6 +568,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PIPE_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4>(c, stream);
         case V_SKINNY: return launch_skinny<T, OutT>(c, stream);
         case V_SKINNY_WIDE: return launch_skinny_wide<T, OutT>(c, stream);
+        case V_SKINNY_RING: return launch_skinny_wide<T, OutT, true>(c, stream);
         case V_REPACK: return launch_repack<T, OutT>(c, stream);
         case V_BT_256_K32_S4: return launch_pipelined<T, OutT, 256, 256, 32, 4, true>(c, stream);
         case V_BT_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4, true>(c, stream);
@@ -591,6 +613,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_GENERIC: return true;
         case V_SKINNY: return skinny_ok(c);
         case V_SKINNY_WIDE: return wide_splits(c) > 0;
+        case V_SKINNY_RING: return ring_splits(c) > 0;
         case V_REPACK: return repack_feasible(c);
         case V_PIPE_256_K32_S4_AP: return apair_ok(c);
         default:

@@ -337,6 +337,187 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_skinny_kernel(SkinnyArgs a
     for (int e = tid * 4; e < BLOCK; e += STEP) *(float4_t*)(part + e) = wave_sum(e);
 }
 
+// ---- the shared-ring skinny kernel -------------------------------------------
+//
+// Same block (64 x 128 outputs over a K range, K split over workgroups) and
+// the same workspace and sum kernel as the wide kernel above, but the waves
+// split the 128 columns instead of K: wave w owns columns 32w .. 32w+31 and
+// every wave reads the same A chunk.  One ring of STAGES stages then serves
+// the whole workgroup (A chunk + B chunk per stage), and the wave partials
+// need no sum.  (Deeper rings, which this layout has room for, measured
+// slower on 64 x 8192 x 8192 than 4 stages of 32-deep chunks.)  A stage
+// is published like the pipelined kernel's: each wave's own copies landed
+// (vmcnt) and its reads of the previous stage retired (lgkmcnt), then one
+// s_barrier.  Copies issued for chunks past the workgroup's range go through
+// a descriptor with no records: they land zeros, touch no memory and keep
+// every wait count the same, so the loop has one form from first to last.
+template <typename T, int KC, int STAGES, typename OutT>
+struct SkinnyRing {
+    static_assert(KC == 32 || KC == 64, "A swizzles exist for 64- and 128-byte rows");
+    static constexpr int WAVES = 4, BM = 64, BN = 128;
+    static constexpr int KSTEPS = KC / 16;
+    static constexpr int A_BYTES = BM * KC * 2;
+    static constexpr int B_BYTES = KC * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LA = A_BYTES / 1024 / WAVES;   // copies per wave per stage
+    static constexpr int LB = B_BYTES / 1024 / WAVES;
+    static constexpr int LPS = LA + LB;
+    static constexpr int A_CHUNKS = KC / 8;             // 16-byte pieces per A row
+    static constexpr int A_ROWS_PER_INST = 64 / A_CHUNKS;
+    static constexpr int B_ROWS_PER_INST = 4;           // 256-byte B rows
+    static constexpr int LDS_BYTES = STAGES * STAGE;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // at the top of chunk c the copies of chunks c+1 .. c+STAGES-2 may still
+    // be in flight
+    static constexpr int VM = (STAGES - 2) * LPS;
+    static_assert(STAGES >= 2 && (STAGES - 1) * LPS < 64, "vmcnt is 6 bits");
+    typedef typename Mfma<T>::frag_t frag_t;
+};
+
+template <typename T, int KC, int STAGES, typename OutT>
+__global__ __launch_bounds__(256, 1) void gemm_skinny_ring_kernel(SkinnyArgs args) {
+    typedef SkinnyRing<T, KC, STAGES, OutT> G;
+    typedef typename G::frag_t frag_t;
+    constexpr int BN = G::BN;
+    constexpr int BLOCK = G::BM * BN;
+    __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
+    BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int splits = args.splits;
+
+    // XCD-aware order, as in the wide kernel
+    int pid = blockIdx.x;
+    const int num = gridDim.x;
+    if ((num & 7) == 0) pid = (pid & 7) * (num >> 3) + (pid >> 3);
+    const int tile = pid / splits, split = pid - tile * splits;
+    const int n0 = tile * BN;
+    const int m0 = blockIdx.y * G::BM;
+    const int batch = blockIdx.z;
+
+    const T* Ab = static_cast<const T*>(args.A) + batch * args.strideA;
+    const T* Bb = static_cast<const T*>(args.B) + batch * args.strideB;
+    const int M = args.M, N = args.N, K = args.K, lda = args.lda, ldb = args.ldb;
+    const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
+    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + N) * 2));
+    const int4_t rsZ = make_rsrc(Bb, 0u);           // every access out of range: zeros
+
+    const int kwg = K / splits;                     // host: kwg % KC == 0
+    const int nchunks = kwg / KC;
+    const int kbase = split * kwg;
+
+    // copy i of wave w moves KiB number w*LA + i of the stage's A chunk, or
+    // w*LB + i of its B chunk; pieces are swizzled as in the wide kernel
+    uint32_t voffA[G::LA];
+#pragma unroll
+    for (int i = 0; i < G::LA; ++i) {
+        const int row = (wave * G::LA + i) * G::A_ROWS_PER_INST + lane / G::A_CHUNKS;
+        const int chunk = (lane % G::A_CHUNKS) ^ swz_a<KC>(row);
+        voffA[i] = (uint32_t)(((m0 + row) * lda + kbase + chunk * 8) * 2);
+    }
+    uint32_t voffB[G::LB];
+#pragma unroll
+    for (int i = 0; i < G::LB; ++i) {
+        const int row = (wave * G::LB + i) * G::B_ROWS_PER_INST + lane / 16;
+        int col = n0 + 8 * ((lane % 16) ^ swz_b(row));
+        if (col >= N) col = N - 8;
+        voffB[i] = (uint32_t)(((kbase + row) * ldb + col) * 2);
+    }
+    const uint32_t astep = KC * 2;
+    const uint32_t bstep = (uint32_t)KC * ldb * 2;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const uint32_t dst = lds0 + (c % STAGES) * G::STAGE;
+        if (c < nchunks) {                          // uniform
+#pragma unroll
+            for (int i = 0; i < G::LA; ++i) dma16(rsA, dst + (wave * G::LA + i) * 1024, voffA[i], c * astep);
+#pragma unroll
+            for (int i = 0; i < G::LB; ++i)
+                dma16(rsB, dst + G::A_BYTES + (wave * G::LB + i) * 1024, voffB[i], c * bstep);
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::LPS; ++i) dma16(rsZ, dst + (wave * G::LPS + i) * 1024 % G::STAGE, 0u, 0u);
+        }
+    };
+
+    // fragment reads: A as in the wide kernel; B block nb = wave
+    uint32_t rdA[G::KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < G::KSTEPS; ++kk) {
+        const int row = lane % 32;
+        rdA[kk] = (uint32_t)(row * KC * 2 + (((kk * 2 + lane / 32) ^ swz_a<KC>(row)) * 16));
+    }
+    const int g = lane / 16, j = lane % 16;
+    const int piece = (4 * wave + 2 * (g % 2) + (j % 4) / 2) ^ swz_b(j / 4);
+    const uint32_t rdB = (uint32_t)(G::A_BYTES + (8 * (g / 2) + j / 4) * BN * 2 + piece * 16 + (j % 2) * 8);
+
+    float16_t acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+        acc[mb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c) __attribute__((always_inline)) {
+        BPT_LDS char* sp = lds + (c % STAGES) * G::STAGE;
+#pragma unroll
+        for (int kk = 0; kk < G::KSTEPS; ++kk) {
+            frag_t a[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) a[mb] = *(BPT_LDS frag_t*)(sp + rdA[kk] + mb * 32 * KC * 2);
+            BPT_LDS char* p = sp + rdB + kk * 16 * BN * 2;
+            short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+            short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 4 * BN * 2));
+            frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<T>::mma32(b, a[mb], acc[mb]);
+        }
+    };
+
+    // chunk c lives in stage c % STAGES; the copies of chunk c + STAGES - 1
+    // refill the stage of chunk c - 1, which every wave has left by the
+    // time the barrier of chunk c passes
+#pragma unroll
+    for (int x = 0; x < STAGES - 1; ++x) issue(x);
+    for (int c = 0; c < nchunks; ++c) {
+        publish<G::VM>();
+        issue(c + STAGES - 1);
+        compute(c);
+    }
+    wait_vm<0>();                                   // the trailing zero copies
+
+    // lane l, register 4q+e of block mb: row mb*32 + l%32, column 32*wave +
+    // 8q + 4(l/32) + e of the block (the B-first MFMA layout)
+    OutT* Cb = static_cast<OutT*>(args.C) + batch * args.strideC;
+    if (splits == 1) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int grow = m0 + mb * 32 + lane % 32;
+                const int gcol = n0 + 32 * wave + 8 * q + 4 * (lane / 32);
+                if (grow < M) {
+                    OutT* dst = Cb + (long long)grow * args.ldc + gcol;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gcol + e < N) dst[e] = cvt_out<OutT>(acc[mb][4 * q + e]);
+                }
+            }
+        return;
+    }
+    const long long blk = ((long long)batch * gridDim.y + blockIdx.y) * args.tiles_n + tile;
+    float* part = args.partial + (blk * splits + split) * BLOCK;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = mb * 32 + lane % 32, col = 32 * wave + 8 * q + 4 * (lane / 32);
+            float4_t v = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
+            *(float4_t*)(part + r * BN + col) = v;
+        }
+}
+
 struct SkinnySumArgs {
     const float* partial;   // [block][split][64][BN] fp32, blocks ordered (batch, row block, column block)
     void* C;

@@ -23,9 +23,10 @@
  * Ownership: A, B and C are DEVICE pointers owned by the caller.  C must not
  * overlap A or B.  The library keeps no per-call state; its one allocation is
  * a workspace used by two paths:
- *   - the split-K path for few rows of A (variant
- *     skinny_64x128_w4_k32_s4_splitk when it splits K over workgroups) keeps
- *     fp32 partial results there (at most 256 MiB);
+ *   - the split-K path for few rows of A (variants
+ *     skinny_64x128_ring_k32_s4_splitk and skinny_64x128_w4_k32_s4_splitk
+ *     when they split K over workgroups) keeps fp32 partial results there
+ *     (at most 256 MiB);
  *   - the repack path (variant repack_pipelined: shapes the pipelined kernels
  *     cannot read in place -- K or N not a multiple of 8, leading dimensions,
  *     batch strides or bases not 16-byte granular -- with at least 2^24

@@ -161,18 +161,21 @@ def test_automatic_variant_choice():
     # K = 64 is one 64-wide tile (two stages need two) and two 32-wide tiles
     # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
-    # few rows of A: the wide skinny kernel (128-column blocks, K split over
-    # 4 or 8 workgroups to reach one workgroup per CU) ...
+    # few rows of A: the shared-ring skinny kernel (128-column blocks, K
+    # split over up to 8 workgroups to reach one workgroup per CU), for any K
+    # that is a multiple of 32 ...
+    ring = v["skinny_64x128_ring_k32_s4_splitk"]
     wide, narrow = v["skinny_64x128_w4_k32_s4_splitk"], v["skinny_64x32_w4_k64_s4"]
-    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == wide
-    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == wide
-    assert pkg.select_variant("f16", 1, 1, 32768, 512, 512, 32768) == wide      # 256 blocks, no split
-    # ... the narrow one (32-column blocks over all of K) when K allows the
-    # wide one too few workgroups: 32 blocks x 2 splits, but 128 narrow ones
-    assert pkg.select_variant("f16", 1, 64, 4096, 1024, 1024, 4096) == narrow
-    # ... and neither when K is too short for either ring (8192 / 128 = 64
-    # wide blocks, K = 768 one split only; narrow needs K >= 1024)
-    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) not in (wide, narrow)
+    assert pkg.select_variant("f16", 1, 64, 8192, 8192, 8192, 8192) == ring
+    assert pkg.select_variant("f16", 1, 16, 4096, 4096, 4096, 4096) == ring
+    assert pkg.select_variant("f16", 1, 1, 32768, 512, 512, 32768) == ring      # 256 blocks, no split
+    assert pkg.select_variant("f16", 1, 64, 4096, 1024, 1024, 4096) == ring     # 32 blocks x 8 splits
+    assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) == ring       # 64 blocks x 4 splits
+    assert pkg.select_variant("f16", 1, 64, 16384, 96, 96, 16384) == ring       # 3 chunks, no split
+    # ... which makes the other two skinny kernels forced-only: each needs
+    # K a multiple of 256 or more, where the ring fits at least as many
+    # splits
+    assert pkg.select_variant("f16", 1, 64, 8192, 8200, 8200, 8192) not in (ring, wide, narrow)
     # N % 8 != 0: column chunks would straddle N in place, so the operands are
     # repacked (B to a width of 8192 resp. 4096, C stored at the true N)
     assert pkg.select_variant("f16", 1, 64, 8190, 8192, 8192, 8190) == repack

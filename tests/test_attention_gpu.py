@@ -100,6 +100,28 @@ def test_zero_scale_exact():
     assert np.array_equal(got.numpy(), ref)
 
 
+@pytest.mark.parametrize("D,Skv", [(256, 16), (128, 8)])
+def test_zero_scale_ragged_exact(D, Skv):
+    """scale 0 with fewer keys than one key block: the masked keys must get
+    weight 0 (not NaN), the rest weight 1, so O is the exact mean of the
+    integer values over a power-of-two count."""
+    say(f"attention zero scale ragged D={D} Skv={Skv}")
+    q = inputs.uniform((2, 40, D), 2071)
+    k = inputs.uniform((2, Skv, D), 2072)
+    v = inputs.small_integers((2, Skv, D), 2073, -3, 3)
+    ref = oracle.attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), 0.0)
+    got = run_attention(q, k, v, 0.0, "f16", True)
+    assert np.array_equal(got.numpy(), ref)
+
+
+def test_zero_scale_ragged_tail():
+    say("attention zero scale, ragged tail of several blocks")
+    q = inputs.uniform((2, 70, 256), 2081)
+    k = inputs.uniform((2, 300, 256), 2082)
+    v = inputs.uniform((2, 300, 256), 2083)
+    check_random(q, k, v, 0.0, "f16", True)
+
+
 def test_rising_maximum_across_blocks():
     """Keys whose logits grow block by block (key j scaled by j/Skv): every
     block raises each row's maximum, many times over 2^8."""

@@ -67,7 +67,7 @@ def check_exact(A, B, dtype, out_fp32, variant=0):
 VARIANTS = ["generic_64x64x16", "pipelined_256x256x64_s2", "pipelined_128x128x64_s2",
             "pipelined_256x256x32_s4", "pipelined_256x256x32_s5", "pipelined_128x128x32_s4",
             "skinny_64x32_w4_k64_s4", "skinny_64x128_w4_k32_s4_splitk", "repack_pipelined",
-            "pipelined_256x256x32_s4_apair"]
+            "pipelined_256x256x32_s4_apair", "skinny_64x128_ring_k32_s4_splitk"]
 # the pipelined variants need K to be a multiple of the K-tile spanning at
 # least as many tiles as ring stages (K >= 160 covers every variant), 16-byte
 # aligned rows (ld % 8 == 0) and N % 8 == 0; M is free and N may end inside
@@ -94,6 +94,10 @@ SHAPES_SKINNY = [(64, 1024, 2048), (37, 320, 2560), (100, 256, 2048), (1, 512, 4
 # (the fewest splits reaching 256 workgroups, else the most that K allows);
 # these two allow S = 1 only (no workspace, no second kernel)
 SHAPES_WIDE_ONLY = [(64, 1024, 512), (3, 136, 640)]
+# the shared-ring skinny variant takes any K that is a multiple of 64 per
+# split: one chunk, and fewer chunks than the ring has stages (the copies
+# past the last chunk read zeros)
+SHAPES_RING_ONLY = [(64, 256, 64), (5, 136, 192), (64, 512, 320)]
 
 
 # the repack route copies A and B zero-padded to K, N rounded up to 8 with
@@ -107,6 +111,8 @@ SHAPES_REPACK = [(300, 201, 256), (257, 65, 129), (129, 129, 250), (64, 1000, 10
 def _shapes(vname):
     if vname == "repack_pipelined":
         return SHAPES_REPACK
+    if vname == "skinny_64x128_ring_k32_s4_splitk":
+        return SHAPES_SKINNY + SHAPES_WIDE_ONLY + SHAPES_RING_ONLY
     if vname.startswith("skinny_64x128"):
         return SHAPES_SKINNY + SHAPES_WIDE_ONLY
     if vname.startswith("skinny"):
@@ -238,12 +244,12 @@ def test_repeat_runs_bitwise_identical():
 
 def test_graph_capture_of_a_split_k_call():
     """A call captured into a graph must not use the per-stream workspace (a
-    graph would keep its address): captured, the wide skinny path runs
+    graph would keep its address): captured, the split-K skinny path runs
     unsplit.  Exact-integer inputs make the split (eager) and unsplit
     (captured) sums bit-identical, so every replay -- with eager calls and
     synchronisations between replays -- must equal the oracle exactly."""
-    M, N, K = 64, 2048, 4096                      # wide skinny kernel, 8 splits when eager
-    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
+    M, N, K = 64, 2048, 4096                      # shared-ring skinny kernel, 8 splits when eager
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["skinny_64x128_ring_k32_s4_splitk"]
     A = inputs.small_integers((M, K), 7501)
     B = inputs.small_integers((K, N), 7502)
     ref = torch.from_numpy(oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"))
@@ -351,13 +357,17 @@ def test_graph_capture_of_a_repack_call():
         assert torch.equal(eager.cpu(), ref), rep_i
 
 
-def test_split_k_workspace_streams_and_growth():
+SPLIT_VARIANTS = ["skinny_64x128_w4_k32_s4_splitk", "skinny_64x128_ring_k32_s4_splitk"]
+
+
+@pytest.mark.parametrize("vname", SPLIT_VARIANTS)
+def test_split_k_workspace_streams_and_growth(vname):
     """The split-K path keeps one workspace per stream: calls on two streams
     in flight together, and a call that needs a larger workspace after a
     smaller one, must each give the result of a lone call, bit for bit (the
     split sums run in a fixed order)."""
-    v = pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
-    shapes = [(64, 256, 2048), (64, 2048, 4096), (32, 1024, 8192)]     # S = 4, 8, 8; growing
+    v = pkg.variants()[vname]
+    shapes = [(64, 256, 2048), (64, 2048, 4096), (32, 1024, 8192)]     # 4-8 splits; growing
     data = []
     for i, (M, N, K) in enumerate(shapes):
         A = inputs.uniform((M, K), 7201 + i, nonzero=True).to(DEV)
@@ -378,13 +388,14 @@ def test_split_k_workspace_streams_and_growth():
         assert torch.equal(C.cpu(), lone[i]), i
 
 
-def test_split_k_repeated_and_interleaved():
-    """Many split-K calls in a row on one stream -- S = 2, 4 and 8 splits,
-    with repack calls that overwrite the shared workspace in between -- must
-    each give the lone call's result bit for bit (the partials are added in
-    split order), and that result meets the oracle."""
-    v = pkg.variants()["skinny_64x128_w4_k32_s4_splitk"]
-    shapes = [(64, 200, 1024), (64, 1024, 2048), (64, 2048, 4096)]      # S = 2, 4, 8
+@pytest.mark.parametrize("vname", SPLIT_VARIANTS)
+def test_split_k_repeated_and_interleaved(vname):
+    """Many split-K calls in a row on one stream -- 2 to 8 splits, with
+    repack calls that overwrite the shared workspace in between -- must each
+    give the lone call's result bit for bit (the partials are added in split
+    order), and that result meets the oracle."""
+    v = pkg.variants()[vname]
+    shapes = [(64, 200, 1024), (64, 1024, 2048), (64, 2048, 4096)]      # wide kernel: S = 2, 4, 8
     rp_A = inputs.uniform((257, 129), 7601, nonzero=True).to(DEV)
     rp_B = inputs.uniform((129, 201), 7602, nonzero=True).to(DEV)
     rp_ref = run(rp_A.cpu(), rp_B.cpu(), "f16", True, pkg.variants()["repack_pipelined"])
