@@ -16,6 +16,7 @@
 #include "../../include/bpt_gemm.h"
 #include "attention.hpp"
 #include "gemm_apair.hpp"
+#include "gemm_persist.hpp"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
@@ -54,7 +55,8 @@ enum Variant {
     V_BT_256_K64_S2 = 13,   // 256x256 tile, BK 64 (128-byte rows of A and Bt), 2 stages
     V_PIPE_256_K32_S4_AP = 14,  // 256x256 tile, BK 32, 4 B stages, A copied in K-tile pairs (whole lines)
     V_SKINNY_RING = 15,     // 64x128 block, waves split the columns, one shared 4-stage ring, + split-sum kernel
-    V_COUNT = 15
+    V_PERSIST = 16,         // persistent 256x128 kernel for K = 128/256, 16-bit C stored during the next tile
+    V_COUNT = 16
 };
 
 bool is_bt_variant(int v) { return v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2; }
@@ -76,11 +78,12 @@ const char* const kVariantNames[] = {
     "pipelined_bt_256x256x64_s2",
     "pipelined_256x256x32_s4_apair",
     "skinny_64x128_ring_k32_s4_splitk",
+    "persistent_256x128x32_shortk",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -265,9 +268,25 @@ bool apair_ok(const Call& c) {
     return c.K % 64 == 0 && c.K >= 192 && pipelined_ok(c, 32, 4, false);
 }
 
+// the persistent short-K kernel: whole 256 x 128 tiles only, K = 128 or
+// 256, 16-bit C, and at least one tile per CU
+bool persist_ok(const Call& c) {
+    if (c.bt || c.out_fp32 || (c.K != 128 && c.K != 256) || c.M % 256 != 0 || c.N % 128 != 0) return false;
+    if (!pipelined_ok(c, 32, 4, false)) return false;
+    // C is stored in 8- and 16-byte pieces without edge checks
+    if (!aligned16(c.C) || (c.ldc * 2) % 16 != 0 || (c.sC * 2) % 16 != 0) return false;
+    const long long total = (c.M / 256) * (c.N / 128) * c.batch;
+    return total >= 256 && total <= kI31;
+}
+
 int choose_pipelined(const Call& c) {
     const long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     const bool big = tiles256 >= 128;
+    // short K over many tiles (8 or more per CU): the persistent kernel
+    // stores each tile's C during the next tile's K-loop; 64 x 4096^2 x 256
+    // 1.17 -> 1.03 ms, K = 128 0.58 -> 0.49 ms on one box, and even at 4
+    // tiles per CU it was 4% slower
+    if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return V_PERSIST;
     // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
     // 1393 -> 1417 against the 32-wide 4-stage kernel on the same box
     if (big && apair_ok(c)) return V_PIPE_256_K32_S4_AP;
@@ -413,6 +432,27 @@ hipError_t launch_apair(const Call& c, hipStream_t stream) {
         hipLaunchKernelGGL((bpt::gemm_apair_kernel<T, OutT>), dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0,
                            stream, a);
     }
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t launch_persist(const Call& c, hipStream_t stream) {
+    bpt::GemmArgs a;
+    a.A = c.A; a.B = c.B; a.C = c.C;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_m = (int)(c.M / 256);
+    a.tiles_n = (int)(c.N / 128);
+    a.group_m = 4;
+    a.c_vec = 1;
+    a.nb = (int)c.N;
+    const int total = (int)((long long)a.tiles_m * a.tiles_n * c.batch);
+    const int grid = total < 256 ? total : 256;            // one workgroup per CU
+    if (c.K == 256)
+        hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a, total);
+    else
+        hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a, total);
     return hipGetLastError();
 }
 
@@ -575,6 +615,9 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_BT_GENERIC: return launch_generic<T, OutT, true>(c, stream);
         case V_BT_256_K64_S2: return launch_pipelined<T, OutT, 256, 256, 64, 2, true>(c, stream);
         case V_PIPE_256_K32_S4_AP: return launch_apair<T, OutT>(c, stream);
+        case V_PERSIST:
+            if constexpr (sizeof(OutT) == 2) return launch_persist<T, OutT>(c, stream);
+            return hipErrorInvalidValue;                      // persist_ok: 16-bit C only
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -616,6 +659,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_SKINNY_RING: return ring_splits(c) > 0;
         case V_REPACK: return repack_feasible(c);
         case V_PIPE_256_K32_S4_AP: return apair_ok(c);
+        case V_PERSIST: return persist_ok(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

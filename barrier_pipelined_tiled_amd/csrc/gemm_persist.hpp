@@ -1,0 +1,279 @@
+// gemm_persist.hpp -- persistent GEMM for short K (C = A * B, B row-major
+// K x N), 16-bit C: one workgroup per CU walks many 256 x 128 output tiles,
+// and the C tile of one output tile is stored while the next one computes.
+//
+// With K = 256 (the batched attention-score shape) a tile is 8 K-tiles of
+// 32, and storing its C takes about as long as computing it (K = 128: 4).  A workgroup
+// per tile pays prologue, K-loop and C stores one after the other, and its
+// CU cannot start the next tile before the stores are acknowledged.  Here
+// the K-tile ring runs on across tile boundaries -- the copies of the next
+// tile start four K-tiles before the current one ends, through that tile's
+// own buffer descriptors -- and the finished accumulators are packed to 16
+// bits into a staging area of LDS beside the ring when the next tile's first
+// products overwrite them.  Each wave then stores its part of the tile in
+// 16-byte row pieces (8 whole 128-byte lines per instruction), spread over
+// the next tile's first 8 K-tiles (all of them when K = 128), right after a
+// publish.  (Stores straight from registers write 8 bytes of 32 different
+// rows per instruction; they measured three times slower than the stores
+// they were meant to hide.)  The last tile takes the usual epilogue.
+//
+// The tile is 256 x 128 (4 waves of 128 x 64) rather than 256 x 256: the
+// ring of 4 stages (96 KiB) and the staged tile (64 KiB) then fill the LDS
+// exactly.  The ring is the pipelined kernel's: 4 stages of one A and one B
+// K-tile, group j+4 copied into the stage tile j leaves, slice 0 in tile j's
+// window and the rest in tile j+1's first k-step; publish(j+1) lets groups
+// j+2 and j+3 stay in flight.
+//
+// Stores share the vmcnt counter with the copies, and only loads are known
+// to complete in issue order among themselves.  Every publish still waits
+// for exactly "all but the younger copies", which is right whatever the
+// stores do: a younger copy completes only after every older one, and the
+// count also covers any store still in flight.  Copies for tiles past the
+// last one go through a descriptor with no records (zeros, no memory
+// traffic), so the loop has one form and every wait count stays constant.
+//
+// Host: M % 256 == 0, N % 128 == 0, K == 32 * NK, 16-byte aligned rows,
+// gridDim.x <= total tiles.
+#pragma once
+#include <utility>
+
+#include "device_common.hpp"
+#include "gemm_pipelined.hpp"
+
+namespace bpt {
+
+template <typename T, typename OutT, int NK>
+__global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int total) {
+    constexpr int BM = 256, BN = 128, BK = 32, STAGES = 4;
+    typedef PipelinedGemm<T, BM, BN, BK, STAGES, 2, 2, OutT, false> G;
+    typedef typename G::frag_t frag_t;
+    static_assert(sizeof(OutT) == 2, "16-bit C: ring and staged tile fill the LDS");
+    static_assert(NK % STAGES == 0, "whole rings per tile");
+    static_assert(G::KS == 2, "one pending slice per group");
+    constexpr int MB = G::MB, NB = G::NB, LPS = G::LPS, DS = G::DSLICE;
+    // staging: each wave's 128 x 64 tile as 128 rows of 128 bytes; 16-byte
+    // chunk q of row r sits at chunk q ^ ((r >> 1) & 7), and rows with bit
+    // 4 set swap the two 8-byte halves of each chunk.  Then the 32 lanes of
+    // an 8-byte write (32 rows, one half chunk) and the 16 lanes of a
+    // 16-byte read (two whole rows) each cover the 64 banks once.
+    constexpr int STG_WAVE = G::TM * G::TN * 2;
+    constexpr int STG_BASE = STAGES * G::STAGE_BYTES;
+    constexpr int LDS_BYTES = STG_BASE + 4 * STG_WAVE;
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+    static_assert(G::TN * 2 == 128, "staging rows of 8 chunks");
+    __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
+    BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / 2;
+    const int wn = wave % 2;
+    const int lda = args.lda, ldb = args.ldb, ldc = args.ldc, K = args.K;
+    const int per = args.tiles_m * args.tiles_n;
+    if ((int)blockIdx.x >= total) return;  // host: gridDim.x <= total; uniform
+
+    // copy offsets relative to the tile's corner (the descriptors start there)
+    uint32_t voffA[G::A_INST_W];
+#pragma unroll
+    for (int i = 0; i < G::A_INST_W; ++i) {
+        const int row = (wave * G::A_INST_W + i) * G::A_ROWS_PER_INST + lane / G::A_CHUNKS;
+        const int chunk = (lane % G::A_CHUNKS) ^ swz_a<BK>(row);
+        voffA[i] = (uint32_t)((row * lda + chunk * 8) * 2);
+    }
+    uint32_t voffB[G::B_INST_W];
+#pragma unroll
+    for (int i = 0; i < G::B_INST_W; ++i) {
+        const int row = (wave * G::B_INST_W + i) * G::B_ROWS_PER_INST + lane / G::B_CHUNKS;
+        const int chunk = (lane % G::B_CHUNKS) ^ swz_b(row);
+        voffB[i] = (uint32_t)((row * ldb + chunk * 8) * 2);
+    }
+    const uint32_t a_step = BK * 2;
+    const uint32_t b_step = (uint32_t)BK * ldb * 2;
+    uint32_t rdA[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        const int row = wm * G::TM + (lane % 32);
+        const int chunk = (ks * 2 + lane / 32) ^ swz_a<BK>(row);
+        rdA[ks] = (uint32_t)((row * BK + chunk * 8) * 2);
+    }
+    uint32_t rdB[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int g = lane / 16, j = lane % 16;
+        const int krow = 8 * (g / 2) + j / 4;
+        const int col = wn * G::TN + nb * 32 + 16 * (g % 2) + 4 * (j % 4);
+        const int chunk = (col / 8) ^ swz_b(krow);
+        rdB[nb] = (uint32_t)(G::A_STAGE * 2 + krow * BN * 2 + chunk * 16 + (col % 8) * 2);
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+
+    // tile number `it` of this workgroup: its batch entry and corner, and
+    // descriptors starting at the corner (no records past the last tile)
+    struct Tile {
+        int batch, m0, n0;
+        int4_t ra, rb;
+    };
+    auto tile_at = [&](int it) __attribute__((always_inline)) {
+        Tile t;
+        const int L = blockIdx.x + it * gridDim.x;
+        if (L < total) {
+            t.batch = L / per;
+            int tm, tn;
+            tile_of(L - t.batch * per, per, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+            t.m0 = tm * BM;
+            t.n0 = tn * BN;
+            const T* a0 = static_cast<const T*>(args.A) + t.batch * args.strideA + (long long)t.m0 * lda;
+            const T* b0 = static_cast<const T*>(args.B) + t.batch * args.strideB + t.n0;
+            t.ra = make_rsrc(a0, (uint32_t)(((BM - 1) * (long long)lda + K) * 2));
+            t.rb = make_rsrc(b0, (uint32_t)(((K - 1) * (long long)ldb + BN) * 2));
+        } else {
+            t.batch = t.m0 = t.n0 = 0;
+            t.ra = t.rb = make_rsrc(args.A, 0u);
+        }
+        return t;
+    };
+
+    // copy i (A copies first) of the group of K-tile kt of tile t, into
+    // stage kt % STAGES
+    auto dma_one = [&](const Tile& t, int i, int kt) __attribute__((always_inline)) {
+        const uint32_t sbase = lds0 + (kt % STAGES) * G::STAGE_BYTES;
+        if (i < G::A_INST_W)
+            dma16(t.ra, sbase + (wave * G::A_INST_W + i) * 1024, voffA[i], kt * a_step);
+        else
+            dma16(t.rb, sbase + G::A_STAGE * 2 + (wave * G::B_INST_W + (i - G::A_INST_W)) * 1024,
+                  voffB[i - G::A_INST_W], kt * b_step);
+    };
+
+    float16_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            acc[i][j] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    typedef OutT out4_t __attribute__((ext_vector_type(4)));
+    BPT_LDS char* stg = lds + STG_BASE + wave * STG_WAVE;
+    auto stg_chunk = [](int r, int q) __attribute__((always_inline)) { return r * 128 + ((q ^ ((r >> 1) & 7)) * 16); };
+
+    frag_t fa[2][MB];
+    short4_t fbl[2][NB], fbh[2][NB];
+    auto read_piece = [&](int st, int ks, int p, int s) __attribute__((always_inline)) {
+        BPT_LDS char* sbase = lds + st * G::STAGE_BYTES;
+        if (p < MB) {
+            fa[s][p] = *(BPT_LDS frag_t*)(sbase + rdA[ks] + p * 32 * BK * 2);
+        } else {
+            const int nb = (p - MB) / 2, h = (p - MB) % 2;
+            BPT_LDS short4_t* q = (BPT_LDS short4_t*)(sbase + rdB[nb] + ks * 16 * BN * 2 + h * 4 * BN * 2);
+            if (h == 0) fbl[s][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q);
+            else fbh[s][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(q);
+        }
+    };
+
+    // One k-step on fragment set s, with the reads of k-step rks of stage
+    // rst into set s^1 and copies [d0, d0 + DS) of the group of K-tile dkt of
+    // tile dt.  FIRST: the tile's first k-step -- each accumulator block is
+    // converted into the staging area just before its first product, which
+    // starts from zero.
+    auto kstep = [&]<bool FIRST>(int s, int rst, int rks, const Tile& dt, int d0, int dkt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < G::NMMA; ++q) {
+#pragma unroll
+            for (int r = 0; r < G::RPM; ++r)
+                if (q * G::RPM + r < G::NREAD) read_piece(rst, rks, q * G::RPM + r, s ^ 1);
+            const int mb = q / NB, nb = q % NB;
+            const frag_t b =
+                __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb], 0, 1, 2, 3, 4, 5, 6, 7));
+            if constexpr (FIRST) {
+                // lane l: row mb*32 + l%32, columns nb*32 + 8g + 4(l/32) .. +3
+                const int r = mb * 32 + (lane % 32);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    out4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = cvt_out<OutT>(acc[mb][nb][4 * g + e]);
+                    *(BPT_LDS out4_t*)(stg + stg_chunk(r, nb * 4 + g) + ((lane / 32) ^ ((r >> 4) & 1)) * 8) = v;
+                }
+                acc[mb][nb] = Mfma<T>::mma32(b, fa[s][mb], float16_t{});
+            } else {
+                acc[mb][nb] = Mfma<T>::mma32(b, fa[s][mb], acc[mb][nb]);
+            }
+#pragma unroll
+            for (int r = 0; r < G::DPQ; ++r) {
+                const int slot = q * G::DPQ + r - G::DOFF;
+                if (slot >= 0 && slot % G::DEVERY == 0 && slot / G::DEVERY < DS)
+                    dma_one(dt, d0 + slot / G::DEVERY, dkt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // The staged previous tile goes out in SLICES slices, one in each of the
+    // next tile's first SLICES K-tiles: slice sl is rows 8 SPS sl .. +8 SPS-1
+    // of the wave tile, 8 rows of 8 chunks per instruction.
+    constexpr int SLICES = NK < 8 ? NK : 8;
+    constexpr int SPS = G::TM / 8 / SLICES;            // store instructions per slice
+    int4_t sv[SPS];
+    auto load_slice = [&](int sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < SPS; ++h) {
+            const int r = (sl * SPS + h) * 8 + lane / 8;
+            int4_t v = *(BPT_LDS int4_t*)(stg + stg_chunk(r, lane % 8));
+            sv[h] = (r & 16) ? int4_t{v[2], v[3], v[0], v[1]} : v;     // undo the half swap
+        }
+    };
+    auto store_slice = [&](int sl, const Tile& pt) __attribute__((always_inline)) {
+        OutT* Cb = static_cast<OutT*>(args.C) + pt.batch * args.strideC;
+#pragma unroll
+        for (int h = 0; h < SPS; ++h) {
+            const int r = (sl * SPS + h) * 8 + lane / 8;
+            OutT* dst = Cb + (long long)(pt.m0 + wm * G::TM + r) * ldc + pt.n0 + wn * G::TN + (lane % 8) * 8;
+            __builtin_nontemporal_store(sv[h], (int4_t*)dst);
+        }
+    };
+
+    // ---- prologue: groups of K-tiles 0 .. 2 and slice 0 of group 3 ----------
+    // (every K-tile's first k-step issues the other slice of group kt+3)
+    Tile cur = tile_at(0);
+    Tile nxt = tile_at(1);
+    Tile prv = cur;                        // the tile in the staging area (none yet)
+#pragma unroll
+    for (int g = 0; g < STAGES - 1; ++g)
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) dma_one(cur, i, g);
+#pragma unroll
+    for (int i = 0; i < DS; ++i) dma_one(cur, i, STAGES - 1);
+    publish<LPS * (STAGES - 2) + DS>();    // group 0 landed for every wave
+#pragma unroll
+    for (int p = 0; p < G::NREAD; ++p) read_piece(0, 0, p, 0);
+
+    // K-tile KT of the current tile: k-step 0 finishes the group of K-tile
+    // KT+3, publish(KT+1), k-step 1 starts the group of K-tile KT+4 (both
+    // possibly of the next tile) in the stage KT just left
+    auto ktile = [&]<int KT>(int it) __attribute__((always_inline)) {
+        constexpr int PK = KT + STAGES - 1, WK = KT + STAGES;
+        const Tile& pt = PK < NK ? cur : nxt;
+        const Tile& wt = WK < NK ? cur : nxt;
+        kstep.template operator()<KT == 0>(0, KT % STAGES, 1, pt, DS, PK % NK);
+        if constexpr (KT == 0) wave_lds_handoff();             // rows staged by other lanes are read below
+        if constexpr (KT < SLICES) load_slice(KT);             // waited for by the publish
+        publish<LPS * (STAGES - 2)>();
+        if constexpr (KT < SLICES) {
+            if (it > 0) store_slice(KT, prv);
+        }
+        kstep.template operator()<false>(1, (KT + 1) % STAGES, 0, wt, 0, WK % NK);
+    };
+
+    for (int it = 0; blockIdx.x + it * gridDim.x < total; ++it) {
+        [&]<int... KT>(std::integer_sequence<int, KT...>) {
+            (ktile.template operator()<KT>(it), ...);
+        }(std::make_integer_sequence<int, NK>{});
+        prv = cur;
+        cur = nxt;
+        nxt = tile_at(it + 2);
+    }
+    // the copies past the last tile read zeros; the epilogue's publish<0>
+    // lets them land before it reuses LDS, then stores the last tile
+    pipelined_epilogue<G, OutT>(args, acc, lds, lane, wave, wm, wn, prv.m0, prv.n0, prv.batch);
+}
+
+}  // namespace bpt

@@ -135,7 +135,14 @@ def test_automatic_variant_choice():
     apair = v["pipelined_256x256x32_s4_apair"]
     assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == apair
     assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == apair
-    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == apair
+    # short K over >= 2048 tiles of 256 x 128 (16-bit C): the persistent kernel
+    persist = v["persistent_256x128x32_shortk"]
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == persist
+    assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == persist
+    assert pkg.select_variant("f16", 4, 4096, 4096, 256, 256, 4096) == persist
+    assert pkg.select_variant("f16", 2, 4096, 4096, 256, 256, 4096) == apair      # 1024 tiles
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096, True) == apair   # fp32 C
+    assert pkg.select_variant("f16", 64, 4096, 4096, 192, 192, 4096) == apair     # K not 128 or 256
     assert pkg.select_variant("f16", 1, 4096, 4096, 192, 192, 4096) == apair
     # K = 160 (five 32-wide tiles): too short for the pair ring, the 4-stage kernel
     assert pkg.select_variant("f16", 1, 4096, 4096, 160, 160, 4096) == big

@@ -223,6 +223,40 @@ def test_batched_small(vname):
     assert np.array_equal(gi.numpy(), oracle.gemm(inputs.bits(Ai), inputs.bits(Bi)))
 
 
+# the persistent short-K kernel: whole 256 x 128 tiles, K = 128 or 256,
+# 16-bit C, at least 256 tiles.  Tile counts 256, 384 (some workgroups walk
+# two tiles, some one), 512, and 512 over 32 batch entries.
+PERSIST_SHAPES = [("f16", 4, 1024, 2048, 256), ("f16", 6, 2048, 1024, 256), ("bf16", 1, 4096, 4096, 256),
+                  ("f16", 32, 512, 1024, 256), ("f16", 6, 2048, 1024, 128), ("bf16", 4, 1024, 2048, 128)]
+
+
+@pytest.mark.parametrize("dtype,batch,M,N,K", PERSIST_SHAPES)
+def test_persistent_parity(dtype, batch, M, N, K):
+    v = pkg.variants()["persistent_256x128x32_shortk"]
+    say(f"[persistent] {dtype} batch={batch} M={M} N={N} K={K}")
+    A = inputs.uniform((batch, M, K), 7701 + M + N, dtype=dtype, nonzero=True)
+    B = inputs.uniform((batch, K, N), 7702 + M + N, dtype=dtype, nonzero=True)
+    check_random(A, B, dtype, False, v)
+    Ai = inputs.small_integers((batch, M, K), 7703, dtype=dtype)
+    Bi = inputs.small_integers((batch, K, N), 7704, dtype=dtype)
+    got = run(Ai, Bi, dtype, False, v)
+    assert np.array_equal(as_bits(got), oracle.encode(oracle.gemm(inputs.bits(Ai), inputs.bits(Bi), dtype), dtype))
+
+
+def test_persistent_repeated_calls():
+    """Back-to-back calls on one stream, the second into a C that the first
+    filled: every call writes every tile once, bit-identical each time."""
+    v = pkg.variants()["persistent_256x128x32_shortk"]
+    A = inputs.uniform((6, 2048, 256), 7711, nonzero=True).to(DEV)
+    B = inputs.uniform((6, 256, 1024), 7712, nonzero=True).to(DEV)
+    outs = [pkg.gemm_ex(A, B, variant=v) for _ in range(4)]
+    C = torch.full((6, 2048, 1024), float("nan"), dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(A, B, C, variant=v)
+    torch.cuda.synchronize()
+    for o in outs[1:] + [C]:
+        assert torch.equal(o, outs[0])
+
+
 def test_batched_entry_point():
     b, M, N, K = 4, 256, 256, 256
     A = inputs.uniform((b, M, K), 7101, lo=-0.5, hi=0.5)
