@@ -2,9 +2,12 @@
 // shapes, e.g. 64 x 8192 x 8192): C (M x N) = A (M x K) * B (K x N).
 //
 // Such a product is bound by streaming B (K x N) from HBM once; A is small and
-// stays in L2.  A workgroup owns a 64 x BN output block (BN = 32 NB columns)
-// over a range of K, and its waves split that range once more ("split-K
-// inside the workgroup").  Each wave streams its share through private LDS
+// stays in L2.  Two workgroup layouts are here.  In gemm_skinny_kernel a
+// workgroup owns a 64 x BN output block (BN = 32 NB columns) over a range of
+// K, and its waves split that range once more ("split-K inside the
+// workgroup").  (gemm_skinny_ring_kernel, further down and the faster of the
+// two, splits the columns over the waves instead and shares one ring; it is
+// described there.)  Each wave streams its share through private LDS
 // rings -- SB stages for B chunks and SA slots for A chunks -- filled by
 // LDS-DMA, so the loop needs no workgroup barrier: a stage is published to the
 // only wave that reads it by that wave's own vmcnt wait (the "bytes pending"
