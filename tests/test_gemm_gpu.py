@@ -243,6 +243,29 @@ def test_persistent_parity(dtype, batch, M, N, K):
     assert np.array_equal(as_bits(got), oracle.encode(oracle.gemm(inputs.bits(Ai), inputs.bits(Bi), dtype), dtype))
 
 
+@pytest.mark.parametrize("K", [256, 128])
+def test_persistent_padded_views_nan_padding(K):
+    """lda > K, ldb > N, ldc > N and batch strides from padded tensors, NaN
+    in every padding element of A and B: the result must be correct and C's
+    padding untouched."""
+    v = pkg.variants()["persistent_256x128x32_shortk"]
+    b, M, N = 4, 1024, 2048                       # 256 tiles of 256 x 128
+    say(f"[persistent padded] b={b} M={M} N={N} K={K}")
+    A = inputs.uniform((b, M, K), 7721 + K, nonzero=True)
+    B = inputs.uniform((b, K, N), 7722 + K, nonzero=True)
+    Ap = torch.full((b, M, K + 8), float("nan"), dtype=torch.float16)
+    Ap[:, :, :K] = A
+    Bp = torch.full((b, K, N + 24), float("nan"), dtype=torch.float16)
+    Bp[:, :, :N] = B
+    Cp = torch.full((b, M, N + 8), 7.0, dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(Ap.to(DEV)[:, :, :K], Bp.to(DEV)[:, :, :N], Cp[:, :, :N], variant=v)
+    torch.cuda.synchronize()
+    Cp = Cp.cpu()
+    assert torch.all(Cp[:, :, N:] == 7.0)
+    m = oracle.compare(Cp[:, :, :N].float().numpy(), oracle.gemm(inputs.bits(A), inputs.bits(B)), K)
+    assert m["ok"], m
+
+
 def test_persistent_repeated_calls():
     """Back-to-back calls on one stream, the second into a C that the first
     filled: every call writes every tile once, bit-identical each time."""
