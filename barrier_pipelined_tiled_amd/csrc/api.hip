@@ -56,10 +56,11 @@ enum Variant {
     V_PIPE_256_K32_S4_AP = 14,  // 256x256 tile, BK 32, 4 B stages, A copied in K-tile pairs (whole lines)
     V_SKINNY_RING = 15,     // 64x128 block, waves split the columns, one shared 4-stage ring, + split-sum kernel
     V_PERSIST = 16,         // persistent 256x128 kernel for K = 128/256, 16-bit C stored during the next tile
-    V_COUNT = 16
+    V_BT_256_K32_S4_AP = 17,  // B transposed: 256x256 tile, A in K-tile pairs, B^T in 4 32-wide stages
+    V_COUNT = 17
 };
 
-bool is_bt_variant(int v) { return v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2; }
+bool is_bt_variant(int v) { return (v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2) || v == V_BT_256_K32_S4_AP; }
 
 const char* const kVariantNames[] = {
     "auto",
@@ -79,11 +80,12 @@ const char* const kVariantNames[] = {
     "pipelined_256x256x32_s4_apair",
     "skinny_64x128_ring_k32_s4_splitk",
     "persistent_256x128x32_shortk",
+    "pipelined_bt_256x256x32_s4_apair",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -250,9 +252,17 @@ bool pipelined_bt_ok(const Call& c, int BK, int STAGES, bool tail) {
 // With B given transposed both operands are copied as rows of K, BK halves
 // each: 64-wide K-tiles move 128-byte segments (whole cache lines) where
 // 32-wide ones move half lines; measured 1143 against 948 TFLOP/s on the
-// 4096 x 4096 x 16384 bf16 shape, 987 against 970 on 4096^3.
+// 4096 x 4096 x 16384 bf16 shape, 987 against 970 on 4096^3.  The A-pair
+// kernel's BT form (A in whole-line pairs, B^T in 32-wide stages) goes
+// further: 4096^3 1160 -> 1276, the long-K shape 1249 -> 1268, against the
+// 64-wide 2-stage kernel.
+bool apair_bt_ok(const Call& c) {
+    return c.K % 64 == 0 && c.K >= 192 && pipelined_bt_ok(c, 32, 4, false);
+}
+
 int choose_bt(const Call& c) {
     const long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
+    if (tiles256 >= 128 && apair_bt_ok(c)) return V_BT_256_K32_S4_AP;
     if (tiles256 >= 128 && pipelined_bt_ok(c, 64, 2, kTailBt<256, 256, 64, 2>)) return V_BT_256_K64_S2;
     if (tiles256 >= 128 && pipelined_bt_ok(c, 32, 4, kTailBt<256, 256, 32, 4>)) return V_BT_256_K32_S4;
     if (pipelined_bt_ok(c, 32, 4, kTailBt<128, 128, 32, 4>)) return V_BT_128_K32_S4;
@@ -411,7 +421,7 @@ hipError_t launch_pipelined(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool BT = false>
 hipError_t launch_apair(const Call& c, hipStream_t stream) {
     bpt::GemmArgs a;
     a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
@@ -429,7 +439,7 @@ hipError_t launch_apair(const Call& c, hipStream_t stream) {
         a.A = static_cast<const T*>(c.A) + b0 * c.sA;
         a.B = static_cast<const T*>(c.B) + b0 * c.sB;
         a.C = static_cast<OutT*>(c.C) + b0 * c.sC;
-        hipLaunchKernelGGL((bpt::gemm_apair_kernel<T, OutT>), dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0,
+        hipLaunchKernelGGL((bpt::gemm_apair_kernel<T, OutT, BT>), dim3((unsigned)tiles, (unsigned)nb), dim3(256), 0,
                            stream, a);
     }
     return hipGetLastError();
@@ -615,6 +625,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_BT_GENERIC: return launch_generic<T, OutT, true>(c, stream);
         case V_BT_256_K64_S2: return launch_pipelined<T, OutT, 256, 256, 64, 2, true>(c, stream);
         case V_PIPE_256_K32_S4_AP: return launch_apair<T, OutT>(c, stream);
+        case V_BT_256_K32_S4_AP: return launch_apair<T, OutT, true>(c, stream);
         case V_PERSIST:
             if constexpr (sizeof(OutT) == 2) return launch_persist<T, OutT>(c, stream);
             return hipErrorInvalidValue;                      // persist_ok: 16-bit C only
@@ -653,6 +664,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_BT_128_K32_S4: return pipelined_bt_ok(c, 32, 4, kTailBt<128, 128, 32, 4>);
         case V_BT_GENERIC: return true;
         case V_BT_256_K64_S2: return pipelined_bt_ok(c, 64, 2, kTailBt<256, 256, 64, 2>);
+        case V_BT_256_K32_S4_AP: return apair_bt_ok(c);
         case V_GENERIC: return true;
         case V_SKINNY: return skinny_ok(c);
         case V_SKINNY_WIDE: return wide_splits(c) > 0;

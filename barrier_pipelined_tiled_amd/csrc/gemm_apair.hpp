@@ -22,6 +22,11 @@
 //   even and one odd group whatever j is, so the wait count is constant.
 //   Only the split of a group's copies over the two k-steps depends on its
 //   parity, so the loop runs two tiles per iteration.
+// * BT: B given transposed (N x K row-major).  Its 32-wide K-tiles are then
+//   K-contiguous rows like A's: copied with A's 32-wide swizzle into the
+//   same 16 KiB B stages and read with one ds_read_b128 per fragment, as in
+//   the pipelined kernel's BT form.  Only A gets whole-line pairs (B pairs
+//   would need another 96 KiB).
 #pragma once
 #include <utility>
 
@@ -30,9 +35,9 @@
 
 namespace bpt {
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool BT = false>
 struct ApairGemm {
-    typedef PipelinedGemm<T, 256, 256, 32, 4, 2, 2, OutT, false> P;   // wave tiles, B layout, epilogue
+    typedef PipelinedGemm<T, 256, 256, 32, 4, 2, 2, OutT, BT> P;      // wave tiles, B layout, epilogue
     static constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, KS = 2;
     static constexpr int MB = P::MB, NB = P::NB, TM = P::TM, TN = P::TN;
     static constexpr int AP_BYTES = BM * 2 * BK * 2;       // one pair stage: 256 rows x 128 bytes
@@ -50,14 +55,14 @@ struct ApairGemm {
     static_assert(LE % KS == 0 && LO % KS == 0, "groups split evenly over the k-steps");
     static_assert((2 * LE + 2 * LO) < 64, "vmcnt is 6 bits");
     static constexpr int NMMA = MB * NB;
-    static constexpr int NREAD = MB + 2 * NB;
+    static constexpr int NREAD = MB + (BT ? 1 : 2) * NB;
     static constexpr int RPM = (NREAD + (NMMA / 2) - 1) / (NMMA / 2);
     typedef typename Mfma<T>::frag_t frag_t;
 };
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool BT = false>
 __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
-    typedef ApairGemm<T, OutT> G;
+    typedef ApairGemm<T, OutT, BT> G;
     typedef typename G::frag_t frag_t;
     constexpr int MB = G::MB, NB = G::NB, BK = G::BK, BN = G::BN, KS = G::KS;
     __shared__ __attribute__((aligned(1024))) char lds_raw[G::LDS_BYTES];
@@ -77,11 +82,13 @@ __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
 
     const T* Ab = static_cast<const T*>(args.A) + batch * args.strideA;
     const T* Bb = static_cast<const T*>(args.B) + batch * args.strideB;
-    const int M = args.M, K = args.K;
+    const int M = args.M, N = args.N, K = args.K;
     const int lda = args.lda, ldb = args.ldb;
     const int4_t rsA = make_rsrc(Ab, (uint32_t)(((M - 1) * (long long)lda + K) * 2));
     const int NB_ = args.nb;
-    const int4_t rsB = make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + NB_) * 2));
+    // BT: B's resource starts at row n0 of B^T, so rows past N read as zero
+    const int4_t rsB = BT ? make_rsrc(Bb + (long long)n0 * ldb, (uint32_t)(((N - n0 - 1) * (long long)ldb + K) * 2))
+                          : make_rsrc(Bb, (uint32_t)(((K - 1) * (long long)ldb + NB_) * 2));
 
     // pair copies: 8 rows of 8 chunks (128 bytes) per instruction, chunk
     // swizzled as the 64-wide K-tile variant's A (rows past M read zero)
@@ -93,18 +100,25 @@ __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
         voffA[i] = (uint32_t)(((m0 + row) * lda + chunk * 8) * 2);
     }
     // B copies as in the 32-wide pipelined kernel (columns past the width
-    // fetch the last in-bounds piece; never stored)
+    // fetch the last in-bounds piece; never stored).  BT: rows of B^T (the
+    // columns of C) in 64-byte pieces, swizzled as A's 32-wide K-tiles.
     uint32_t voffB[G::B_INST];
 #pragma unroll
     for (int i = 0; i < G::B_INST; ++i) {
-        const int row = (wave * G::B_INST + i) * 2 + lane / 32;
-        const int chunk = (lane % 32) ^ swz_b(row);
-        int col = n0 + chunk * 8;
-        if (col >= NB_) col = NB_ - 8;
-        voffB[i] = (uint32_t)((row * ldb + col) * 2);
+        if constexpr (BT) {
+            const int row = (wave * G::B_INST + i) * G::P::B_ROWS_PER_INST + lane / G::P::B_CHUNKS;
+            const int chunk = (lane % G::P::B_CHUNKS) ^ swz_a<BK>(row);
+            voffB[i] = (uint32_t)((row * ldb + chunk * 8) * 2);
+        } else {
+            const int row = (wave * G::B_INST + i) * 2 + lane / 32;
+            const int chunk = (lane % 32) ^ swz_b(row);
+            int col = n0 + chunk * 8;
+            if (col >= NB_) col = NB_ - 8;
+            voffB[i] = (uint32_t)((row * ldb + col) * 2);
+        }
     }
     const uint32_t pair_step = 2 * BK * 2;                 // bytes of A per pair
-    const uint32_t b_step = (uint32_t)BK * ldb * 2;        // bytes of B per K-tile
+    const uint32_t b_step = BT ? (uint32_t)BK * 2 : (uint32_t)BK * ldb * 2;   // bytes of B per K-tile
 
     // A block mb of K-tile parity t, k-step ks: row wm*TM + mb*32 + l%32,
     // logical chunk 4t + 2ks + l/32 of the 128-byte row, swizzled
@@ -126,6 +140,15 @@ __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
         const int col = wn * G::TN + nb * 32 + 16 * (g % 2) + 4 * (j % 4);
         const int chunk = (col / 8) ^ swz_b(krow);
         rdB[nb] = (uint32_t)(G::B_BASE + krow * BN * 2 + chunk * 16 + (col % 8) * 2);
+    }
+    // BT: B block nb, k-step ks is read like A: row (column of C) wn*TN +
+    // nb*32 + lane%32 of the [BN][BK] stage, k ks*16 + 8*(lane/32)
+    uint32_t rdBt[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int row = wn * G::TN + (lane % 32);
+        const int chunk = (ks * 2 + lane / 32) ^ swz_a<BK>(row);
+        rdBt[ks] = (uint32_t)(G::B_BASE + (row * BK + chunk * 8) * 2);
     }
 
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
@@ -149,11 +172,14 @@ __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
 
     frag_t fa[2][MB];
     short4_t fbl[2][NB], fbh[2][NB];
+    frag_t fbt[2][NB];                     // BT: B in one read
 
     // LDS read p of k-step ks of a tile (A pair stage ast, parity t; B stage bst) into set s
     auto read_piece = [&](int ast, int t, int bst, int ks, int p, int s) __attribute__((always_inline)) {
         if (p < MB) {
             fa[s][p] = *(BPT_LDS frag_t*)(lds + ast * G::AP_BYTES + rdA[t][ks] + p * 32 * 128);
+        } else if constexpr (BT) {
+            fbt[s][p - MB] = *(BPT_LDS frag_t*)(lds + bst * G::B_BYTES + rdBt[ks] + (p - MB) * 32 * BK * 2);
         } else {
             const int nb = (p - MB) / 2, h = (p - MB) % 2;
             BPT_LDS short4_t* q = (BPT_LDS short4_t*)(lds + bst * G::B_BYTES + rdB[nb] + ks * 16 * BN * 2 + h * 4 * BN * 2);
@@ -176,7 +202,11 @@ __global__ __launch_bounds__(256, 1) void gemm_apair_kernel(GemmArgs args) {
                     if (q * G::RPM + r < G::NREAD) read_piece(rast, rt, rbst, rks, q * G::RPM + r, s ^ 1);
             }
             const int mb = q / NB, nb = q % NB;
-            const frag_t b = __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb], 0, 1, 2, 3, 4, 5, 6, 7));
+            frag_t b;
+            if constexpr (BT)
+                b = fbt[s][nb];
+            else
+                b = __builtin_bit_cast(frag_t, __builtin_shufflevector(fbl[s][nb], fbh[s][nb], 0, 1, 2, 3, 4, 5, 6, 7));
             acc[mb][nb] = Mfma<T>::mma32(b, fa[s][mb], acc[mb][nb]);
             if constexpr (SLICE > 0) {
                 const int slot = q - DOFF;

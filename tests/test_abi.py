@@ -209,10 +209,12 @@ def test_bt_layout_entry_point(L):
                    v["pipelined_bt_256x256x32_s4"], None)
     assert st == pkg.BPT_ERR_UNSUPPORTED
     # automatic choice for the transposed layout
-    # 64-wide K-tiles when K allows them (whole 128-byte rows per copy) ...
-    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x64_s2"]
+    # A in whole-line K-tile pairs when K % 64 == 0 and K >= 192 ...
+    assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x32_s4_apair"]
     # ... and N need not be a multiple of 8 here
-    assert pkg.select_variant("f16", 1, 4096, 4095, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x64_s2"]
+    assert pkg.select_variant("f16", 1, 4096, 4095, 4096, 4096, 4096, bt=True) == v["pipelined_bt_256x256x32_s4_apair"]
+    # K = 128: too short for the pairs, 64-wide K-tiles (whole 128-byte rows) in 2 stages
+    assert pkg.select_variant("f16", 1, 4096, 4096, 128, 128, 128, bt=True) == v["pipelined_bt_256x256x64_s2"]
     # K = 4104: no 64-wide tiling, the 32-wide one with a tail
     assert pkg.select_variant("f16", 1, 4096, 4096, 4104, 4104, 4104, bt=True) == v["pipelined_bt_256x256x32_s4"]
     assert pkg.select_variant("f16", 1, 256, 200, 256, 256, 256, bt=True) == v["pipelined_bt_128x128x32_s4"]

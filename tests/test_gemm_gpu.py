@@ -558,7 +558,7 @@ def test_full_size_exact_integers(name):
 # ----------------------------------------------------------------------------
 
 BT_VARIANTS = ["pipelined_bt_256x256x32_s4", "pipelined_bt_128x128x32_s4", "generic_bt_64x64x16",
-               "pipelined_bt_256x256x64_s2"]
+               "pipelined_bt_256x256x64_s2", "pipelined_bt_256x256x32_s4_apair"]
 # any N (rows of Bt past N read as zero): 201, 7 and 520 are not multiples
 # of 8; K tails of 8 (136 = 4 x 32 + 8, 1032) as on the other layout
 SHAPES_BT = [(256, 256, 256), (300, 201, 192), (33, 520, 136), (129, 136, 256), (512, 384, 1032), (1, 7, 128)]
@@ -570,6 +570,8 @@ def _bt_shapes(vname):
         return SHAPES_BT + SHAPES_BT_GENERIC_ONLY
     if "x64_s2" in vname:                 # 64-wide K-tiles, no tail stage: K % 64 == 0, K >= 128
         return [(M, N, K) for (M, N, K) in SHAPES_BT if K % 64 == 0] + [(200, 264, 1088)]
+    if "apair" in vname:                  # A in K-tile pairs: K % 64 == 0, K >= 192, no tail
+        return [(M, N, K) for (M, N, K) in SHAPES_BT if K % 64 == 0 and K >= 192] + [(200, 264, 1088), (257, 1000, 384)]
     return SHAPES_BT
 
 
@@ -645,7 +647,7 @@ def test_bt_full_size_sampled_and_exact():
     """4096^3 with B given transposed (the automatic choice), sampled against
     the oracle: random inputs by tolerance, small integers bit for bit."""
     M = N = K = 4096
-    assert pkg.select_variant("f16", 1, M, N, K, K, K, bt=True) == pkg.variants()["pipelined_bt_256x256x64_s2"]
+    assert pkg.select_variant("f16", 1, M, N, K, K, K, bt=True) == pkg.variants()["pipelined_bt_256x256x32_s4_apair"]
     b, r, c = _sample_positions(1, M, N, 2048, 29)
     for kind in ("random", "exact"):
         if kind == "random":
