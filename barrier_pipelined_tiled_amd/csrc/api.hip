@@ -294,11 +294,11 @@ int choose_pipelined(const Call& c) {
     const bool big = tiles256 >= 128;
     // short K over many tiles (8 or more per CU): the persistent kernel
     // stores each tile's C during the next tile's K-loop; 64 x 4096^2 x 256
-    // 1.17 -> 1.03 ms, K = 128 0.58 -> 0.49 ms on one box, and even at 4
+    // 1.17 -> 1.03 ms, K = 128 0.58 -> 0.49 ms on one machine, and even at 4
     // tiles per CU it was 4% slower
     if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return V_PERSIST;
     // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
-    // 1393 -> 1417 against the 32-wide 4-stage kernel on the same box
+    // 1393 -> 1417 against the 32-wide 4-stage kernel on the same machine
     if (big && apair_ok(c)) return V_PIPE_256_K32_S4_AP;
     if (big && pipelined_ok(c, 32, 4, variant_tail(V_PIPE_256_K32_S4))) return V_PIPE_256_K32_S4;
     if (pipelined_ok(c, 32, 4, variant_tail(V_PIPE_128_K32_S4))) return V_PIPE_128_K32_S4;

@@ -12,7 +12,7 @@ between two device synchronisations.  The kernel time is measured with HIP
 events recorded on the stream the kernels are launched on.  After the pause
 the clock takes some 20 ms of load to come back up, so short timed blocks
 read low (4096^3: 1090 TFLOP/s over 200 calls, 1190 over 1000, 1216 over
-3000 on the same box).
+3000 on the same machine).
 
 The JSON line also carries
 * roofline: algorithmic flops (or bytes, for the memory-bound shape) per
