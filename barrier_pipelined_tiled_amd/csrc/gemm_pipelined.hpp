@@ -85,17 +85,20 @@ __device__ inline void tile_of(int pid, int num, int tiles_m, int tiles_n, int g
 // fixes where a lane's 16 bytes land (base + 16*lane), so the swizzle is
 // applied by choosing which global chunk each lane fetches.
 //
-// A rows are BK halves.  ds_read_b128 of 32 consecutive rows at one k-chunk
-// must spread over the banks whether the hardware serves 8 lanes (128 B) or
-// 16 lanes (256 B) of a 16-byte read per cycle:
+// A rows are BK halves, read by ds_read_b128 as 32 consecutive rows at one
+// k-chunk (lanes 0-31) and the next chunk of the same rows (lanes 32-63):
 //   BK = 64 (8 chunks, 128 B rows): chunk ^ ((row & 7) ^ ((row >> 3) & 1))
-//   BK = 32 (4 chunks,  64 B rows): chunk ^ (((row >> 1) ^ (row >> 3)) & 3)
+//   BK = 32 (4 chunks,  64 B rows): chunk ^ ((row >> 2) & 3)
+// Both were measured conflict-free (SQ_LDS_BANK_CONFLICT 0, 4 LDS cycles
+// per instruction) by a probe running the read pattern alone.  For 64-byte
+// rows, chunk ^ (((row >> 1) ^ (row >> 3)) & 3), which a 64-bank model calls
+// conflict-free, measured 2-way (8 cycles), and no swizzle 4-way.
 template <int BK>
 __device__ inline int swz_a(int row);
 template <>
 __device__ inline int swz_a<64>(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 template <>
-__device__ inline int swz_a<32>(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ inline int swz_a<32>(int row) { return (row >> 2) & 3; }
 
 // B rows are BN halves (>= 16 chunks).  ds_read_b64_tr_b16 makes each
 // 16-lane group read 4 consecutive k rows x 32 bytes; f(k & 3) from
