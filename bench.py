@@ -18,13 +18,19 @@ The JSON line also carries
 * roofline: algorithmic flops (or bytes, for the memory-bound shape) per
   launch over the average launch duration, against MI355X's dense peak;
 * cpu_baseline: the CPU oracle timed on a bounded sample (leading rows of
-  the same product) on the host cores, scaled to the same unit.
+  the same product) on the host cores, scaled to the same unit;
+* clocks: amd-smi readings of the shader clock (mean over the XCDs), the
+  memory clock and the socket power before the warm-up, while the same
+  steps run again after the timed block, and after them (none of it inside
+  the timed block; `--no-clocks` skips it).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import shutil
+import subprocess
 import sys
 import time
 
@@ -33,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16_TFLOPS = 2516.6     # 256 CU x 2048 fp16 FMA/clk/CU x 2 x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+NOMINAL_GFX_MHZ = 2400           # the shader clock the dense peak above is quoted at
 
 METRIC = "fp16 GEMM TFLOPS at M=N=K=4096 (1 MI355X); % of dense FP16 MFMA peak"
 
@@ -155,6 +162,76 @@ def record_traffic(run_dir: str, path: str | None = None) -> None:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(f"wrote {path}: {sorted(entries)} at source {sha}")
+
+
+def parse_smi(text: str) -> dict:
+    """Shader clock (mean over the XCDs' gfx clocks), memory clock and socket
+    power of GPU 0 from `amd-smi metric -g 0 -c -p --json` output."""
+    d = json.loads(text)
+    g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+    clk = g.get("clock", {})
+
+    def val(x):
+        return x.get("value") if isinstance(x, dict) else None
+
+    gfx = [val(v.get("clk")) for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+    gfx = [x for x in gfx if isinstance(x, (int, float))]
+    mem = clk.get("mem_0", {})
+    return {
+        "gfx_mhz": round(sum(gfx) / len(gfx)) if gfx else None,
+        "mem_mhz": val(mem.get("clk")) if isinstance(mem, dict) else None,
+        "power_w": val(g.get("power", {}).get("socket_power")),
+    }
+
+
+def smi_start():
+    """amd-smi started as a child process (the reading runs beside this one)."""
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    try:
+        return subprocess.Popen([exe, "metric", "-g", "0", "-c", "-p", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+
+
+def smi_finish(proc) -> dict | None:
+    if proc is None:
+        return None
+    try:
+        out, _ = proc.communicate(timeout=30)
+        return parse_smi(out)
+    except Exception as exc:                   # a reading is a report, never a failure
+        proc.kill()
+        return {"error": str(exc)[:120]}
+
+
+def clocks_under_load(torch, step, settle_s: float = 2.0, max_s: float = 20.0) -> dict | None:
+    """One amd-smi reading taken while the same steps keep the GPU busy: the
+    steps run settle_s seconds first (the power reading is an average over a
+    window), then on until amd-smi returns."""
+    t0 = time.perf_counter()
+    i = 0
+
+    def burst():
+        nonlocal i
+        for _ in range(64):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+
+    while time.perf_counter() - t0 < settle_s:
+        burst()
+    proc = smi_start()
+    if proc is None:
+        return None
+    while proc.poll() is None and time.perf_counter() - t0 < max_s:
+        burst()
+    r = smi_finish(proc)
+    if isinstance(r, dict):
+        r["load_s"] = round(time.perf_counter() - t0, 2)
+    return r
 
 
 def time_steps(torch, step, args, stream):
@@ -317,6 +394,7 @@ def main():
     ap.add_argument("--variant", type=int, default=0, help="GEMM variant, 0 = automatic choice")
     ap.add_argument("--sleep", type=float, default=5.0, help="pause before timing (s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock and power readings")
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
                     help="GEMM only.  kn: B is K x N (the workloads' layout); nt: the same B handed "
                          "over transposed (N x K) through gemm_ex_bt")
@@ -351,7 +429,12 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident in HBM")
 
+    clk_before = None if args.no_clocks else smi_finish(smi_start())
     ms_per_step, kernel_ms, spread = time_steps(torch, step, args, stream)
+    clocks = None
+    if not args.no_clocks:
+        clocks = {"nominal_gfx_mhz": NOMINAL_GFX_MHZ, "before": clk_before,
+                  "under_load": clocks_under_load(torch, step), "after": smi_finish(smi_start())}
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     roof = roofline(w.flops, w.compulsory_bytes, kernel_ms)
     roof["traffic"] = measured_traffic(w.name, kernel)
@@ -375,6 +458,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_call": spread,
+        "clocks": clocks,
     }
     print(json.dumps(out), flush=True)
 

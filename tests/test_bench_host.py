@@ -83,3 +83,21 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_parse_smi_reads_shader_memory_clock_and_power():
+    # the shape of `amd-smi metric -g 0 -c -p --json` on ROCm 7.2: one gfx
+    # clock per XCD, memory clocks, socket power
+    sample = {"gpu_data": [{"gpu": 0,
+                            "power": {"socket_power": {"value": 1180, "unit": "W"}},
+                            "clock": {**{f"gfx_{i}": {"clk": {"value": 1700 + 10 * i, "unit": "MHz"}}
+                                         for i in range(8)},
+                                      "mem_0": {"clk": {"value": 2000, "unit": "MHz"}},
+                                      "vclk_0": {"clk": {"value": 29, "unit": "MHz"}}}}]}
+    r = bench.parse_smi(json.dumps(sample))
+    assert r == {"gfx_mhz": 1735, "mem_mhz": 2000, "power_w": 1180}
+
+
+def test_parse_smi_tolerates_missing_fields():
+    r = bench.parse_smi(json.dumps({"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": "N/A"}}}]}))
+    assert r == {"gfx_mhz": None, "mem_mhz": None, "power_w": None}
