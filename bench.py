@@ -78,6 +78,18 @@ def measured_traffic(workload: str, kernel: str):
     return int(round(kib * 1024))
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, A, B, budget_s: float = 15.0, min_s: float = 10.0):
     """Time the oracle on the first R rows of A times all of B (set 0), R
     grown until one call takes at least min_s seconds (or covers all rows)."""
@@ -103,6 +115,7 @@ def cpu_baseline(w, A, B, budget_s: float = 15.0, min_s: float = 10.0):
         "value": flops / t / 1e12,
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of A ({rows}x{K}) times B ({K}x{N}), "
                   f"{w.dtype}, fp64 accumulation, {t:.1f} s",
@@ -350,6 +363,7 @@ def attention_cpu_baseline(w, q, k, v, budget_s: float = 15.0, min_s: float = 10
         "value": flops / t / 1e12,
         "unit": "TFLOPS",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"the first {rows} query rows (heads 0..{(rows - 1) // w.Sq}), each against the "
                   f"{w.Skv} keys of its head, D = {w.D}, {w.dtype}, fp64, {t:.1f} s",
