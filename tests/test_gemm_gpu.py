@@ -552,6 +552,70 @@ def test_full_size_exact_integers(name):
         assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
 
 
+def _sampled_block(A, B, C, seed, n=16):
+    """Rows and columns of C (random ones plus the first and last) and the
+    oracle's fp32 values of that block, from the CPU operands A (M,K), B (K,N)."""
+    M, N = C.shape
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.integers(0, M, n), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, N, n), [0, N - 1]]))
+    ref = oracle.gemm(inputs.bits(A[torch.from_numpy(rows)]), inputs.bits(B[:, torch.from_numpy(cols)]), "f16")
+    got = C[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu()
+    return got, ref
+
+
+def test_operand_over_2gib_runs_on_64bit_offsets():
+    """B of 2^20 x 1024 fp16 spans 2 GiB, past the 32-bit byte offsets of the
+    buffer descriptors: every fast variant must refuse the call and the
+    automatic choice must take the guarded kernel, whose offsets are 64-bit.
+    Integer inputs make the sampled outputs exact."""
+    M, N, K = 96, 1024, 1 << 20
+    say(f"[max-size] B extent {K * N * 2} bytes, M={M} N={N} K={K}")
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["generic_64x64x16"]
+    A = inputs.small_integers((M, K), 8101)
+    B = inputs.small_integers((K, N), 8102)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    for vname in ("pipelined_256x256x32_s4_apair", "pipelined_256x256x32_s4", "skinny_64x128_ring_k32_s4_splitk",
+                  "repack_pipelined"):
+        with pytest.raises(pkg.GemmError) as e:
+            pkg.gemm_ex(Ad, Bd, out_fp32=True, variant=pkg.variants()[vname])
+        assert e.value.status == pkg.BPT_ERR_UNSUPPORTED, vname
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    pkg.gemm_ex(Ad, Bd, C, out_fp32=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(C).any().item()
+    got, ref = _sampled_block(A, B, C, 8103)
+    assert np.array_equal(got.numpy(), ref)
+    del Ad, Bd, C
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("out_fp32,vname", [(False, "persistent_256x128x32_shortk"),
+                                            (True, "pipelined_256x256x32_s4_apair")])
+def test_single_output_over_2gib(out_fp32, vname):
+    """One C of 32768 x 32768 (2 GiB in fp16, 4 GiB in fp32) from the fast
+    kernels: their C addresses are 64-bit, so every element is written (C is
+    filled with NaN first) and sampled outputs equal the oracle bit for bit
+    (integer inputs, |C| <= 1024)."""
+    M = N = 32768
+    K = 256
+    say(f"[max-size] C {M}x{N} out_fp32={out_fp32} ({vname})")
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, out_fp32) == pkg.variants()[vname]
+    A = inputs.small_integers((M, K), 8201)
+    B = inputs.small_integers((K, N), 8202)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32 if out_fp32 else torch.float16, device=DEV)
+    pkg.gemm_ex(A.to(DEV), B.to(DEV), C, out_fp32=out_fp32)
+    torch.cuda.synchronize()
+    assert not torch.isnan(C).any().item()
+    got, ref = _sampled_block(A, B, C, 8203)
+    if out_fp32:
+        assert np.array_equal(got.numpy(), ref)
+    else:
+        assert np.array_equal(as_bits(got), oracle.encode(ref, "f16"))
+    del C
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # B given transposed (gemm_ex_bt): C = A * Bt^T, Bt N x K row-major.  The
 # oracle takes B = Bt^T, transposed on the host (16-bit patterns, exact).
