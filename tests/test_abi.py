@@ -253,6 +253,7 @@ def _attn(L, dtype=0, BH=2, Sq=128, Skv=64, D=256, Q=FAKE, ldq=256, sQ=0, K=FAKE
     (dict(ldk=260), pkg.BPT_ERR_UNSUPPORTED),                                 # row not 16-byte granular
     (dict(sO=12), pkg.BPT_ERR_UNSUPPORTED),
     (dict(Skv=1 << 22, ldk=256), pkg.BPT_ERR_UNSUPPORTED),                     # head's K extent >= 2^31 bytes
+    (dict(Skv=4194240), pkg.BPT_ERR_UNSUPPORTED),          # the first Skv whose K (+64 rows) reaches 2^31 bytes
 ])
 def test_attention_rejections(L, kw, status):
     assert _attn(L, **kw) == status, kw

@@ -217,6 +217,28 @@ def test_small_workload_whole():
         check_random(w.make_q(j), w.make_k(j), w.make_v(j), w.scale, w.dtype, w.out_fp32)
 
 
+def test_key_extent_near_2gib():
+    """Two heads of 4,194,000 keys at D = 256.  Each head's K and V, plus
+    the block of rows a ragged tail may read past the end, span just under
+    2^31 bytes, the most the 32-bit buffer offsets take (4,194,240 keys are
+    refused).  The second head starts more than 2^31 bytes past the base,
+    and the last block holds 16 keys.  Sampled rows against the oracle."""
+    BH, Sq, Skv, D = 2, 64, 4194000, 256
+    assert (Skv + 64) * D * 2 < 2**31 - 1 and (4194240 + 64) * D * 2 > 2**31 - 1
+    say(f"attention BH={BH} Sq={Sq} Skv={Skv} D={D} (K, V {BH * Skv * D * 2} bytes each)")
+    q = inputs.uniform((BH, Sq, D), 2701, lo=-0.5, hi=0.5)
+    k = inputs.uniform((BH, Skv, D), 2702, lo=-0.5, hi=0.5)
+    v = inputs.uniform((BH, Skv, D), 2703)
+    scale = 1.0 / 16
+    got = run_attention(q, k, v, scale, "f16", True)
+    assert torch.isfinite(got).all()
+    bi = np.array([0, 0, 1, 1], dtype=np.int64)
+    ri = np.array([0, Sq - 1, 0, 37], dtype=np.int64)
+    ref = oracle.attention(inputs.bits(q), inputs.bits(k), inputs.bits(v), scale, "f16", rows=(bi, ri))
+    m = oracle.compare_attention(got[bi, ri].numpy(), ref)
+    assert m["ok"], m
+
+
 def test_full_size_sampled():
     """The benchmark's shape (64 heads x 4096 queries x 4096 keys, D = 256):
     every output finite, and 64 sampled rows (each head's first or last row
