@@ -217,6 +217,10 @@ def smi_finish(proc) -> dict | None:
         return parse_smi(out)
     except Exception as exc:                   # a reading is a report, never a failure
         proc.kill()
+        try:
+            proc.communicate(timeout=5)
+        except Exception:
+            pass
         return {"error": str(exc)[:120]}
 
 

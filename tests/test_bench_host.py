@@ -101,3 +101,11 @@ def test_parse_smi_reads_shader_memory_clock_and_power():
 def test_parse_smi_tolerates_missing_fields():
     r = bench.parse_smi(json.dumps({"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": "N/A"}}}]}))
     assert r == {"gfx_mhz": None, "mem_mhz": None, "power_w": None}
+
+
+def test_smi_finish_reports_a_bad_reading_instead_of_raising():
+    import subprocess
+    proc = subprocess.Popen([sys.executable, "-c", "print('not json')"], stdout=subprocess.PIPE, text=True)
+    r = bench.smi_finish(proc)
+    assert set(r) == {"error"}
+    assert bench.smi_finish(None) is None
