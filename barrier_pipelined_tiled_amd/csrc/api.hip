@@ -390,6 +390,14 @@ int choose(const Call& c) {
         const int S = ring_splits(c);
         if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
         if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
+    } else if (c.M <= 128 && (c.N + 127) / 128 * c.batch < 256) {
+        // two row blocks of the ring kernel (B streamed once per block) beat
+        // 128 x 128 tiles that give fewer than one workgroup per CU: 128 x
+        // 8192^2 0.0627 -> 0.0393 ms, 96 x 8192^2 0.0539 -> 0.0371, 128 x
+        // 4096^2 0.0315 -> 0.0152 on one machine; at 192 and 256 rows the
+        // two were even
+        const int S = ring_splits(c);
+        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
     }
     const int v = choose_pipelined(c);
     if (v != V_GENERIC) return v;

@@ -179,6 +179,14 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 64, 4096, 1024, 1024, 4096) == ring     # 32 blocks x 8 splits
     assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) == ring       # 64 blocks x 4 splits
     assert pkg.select_variant("f16", 1, 64, 16384, 96, 96, 16384) == ring       # 3 chunks, no split
+    # up to 128 rows (two row blocks) while 128 x 128 tiles would leave CUs
+    # idle; from 129 rows, or with 256 or more such tiles, the pipelined kernels
+    assert pkg.select_variant("f16", 1, 128, 8192, 8192, 8192, 8192) == ring
+    assert pkg.select_variant("f16", 1, 96, 8192, 8192, 8192, 8192) == ring
+    assert pkg.select_variant("f16", 1, 128, 4096, 4096, 4096, 4096) == ring
+    assert pkg.select_variant("f16", 1, 129, 8192, 8192, 8192, 8192) == v["pipelined_128x128x32_s4"]
+    assert pkg.select_variant("f16", 1, 192, 8192, 8192, 8192, 8192) == v["pipelined_128x128x32_s4"]
+    assert pkg.select_variant("f16", 1, 128, 32768, 4096, 4096, 32768) == v["pipelined_256x256x32_s4_apair"]
     # ... which makes the other two skinny kernels forced-only: each needs
     # K a multiple of 256 or more, where the ring fits at least as many
     # splits
