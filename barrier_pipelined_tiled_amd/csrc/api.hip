@@ -21,6 +21,7 @@
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
 #include "repack.hpp"
+#include "splitk.hpp"
 
 namespace {
 
@@ -57,7 +58,8 @@ enum Variant {
     V_SKINNY_RING = 15,     // 64x128 block, waves split the columns, one shared 4-stage ring, + split-sum kernel
     V_PERSIST = 16,         // persistent 256x128 kernel for K = 128/256, 16-bit C stored during the next tile
     V_BT_256_K32_S4_AP = 17,  // B transposed: 256x256 tile, A in K-tile pairs, B^T in 4 32-wide stages
-    V_COUNT = 17
+    V_SPLITK = 18,          // few output tiles: K split over the pipelined kernel's batch, + split-sum kernel
+    V_COUNT = 18
 };
 
 bool is_bt_variant(int v) { return (v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2) || v == V_BT_256_K32_S4_AP; }
@@ -81,11 +83,12 @@ const char* const kVariantNames[] = {
     "skinny_64x128_ring_k32_s4_splitk",
     "persistent_256x128x32_shortk",
     "pipelined_bt_256x256x32_s4_apair",
+    "splitk_pipelined",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -368,6 +371,42 @@ bool repack_ok(const Call& c) {
     return (double)c.batch * c.M * c.N * c.K >= (double)(1 << 24) && repack_feasible(c);
 }
 
+// ---- split-K for the pipelined kernels ----------------------------------------
+// An output of at most 128 tiles of 128 x 128 (fewer than half the CUs get
+// a workgroup) is computed as S K-ranges at once: the pipelined kernel runs
+// with the ranges as its batch (A advanced by K/S columns, B by K/S rows per
+// entry) into fp32 partials in the stream's workspace, and splitk_sum_kernel
+// adds them in split order.  S is the largest power of two (at most 8) that
+// keeps the tiles within one workgroup per CU, with K/S a multiple of 64 and
+// at least 256.
+Call splitk_call(const Call& c, int S, void* ws) {
+    Call p = c;
+    p.batch = S;
+    p.K = c.K / S;
+    p.sA = p.K;
+    p.sB = p.K * c.ldb;
+    p.C = ws;
+    p.ldc = c.N;
+    p.sC = c.M * c.N;
+    p.out_fp32 = 1;
+    return p;
+}
+
+int splitk_splits(const Call& c) {
+    if (c.bt || c.batch != 1 || c.M <= 128 || c.K <= 0 || c.N % 8 != 0) return 0;
+    const long long tiles = ((c.M + 127) / 128) * ((c.N + 127) / 128);
+    alignas(256) static char probe[256];           // stands in for the workspace
+    int best = 0;
+    for (int S = 2; S <= 8; S *= 2) {
+        if (tiles * S > 256) break;
+        if (c.K % (64LL * S) != 0 || c.K / S < 256) break;
+        if ((long long)S * c.M * c.N * 4 > kWorkspaceMax) break;
+        if (choose_pipelined(splitk_call(c, S, probe)) == V_GENERIC) break;
+        best = S;
+    }
+    return best;
+}
+
 bool variant_tail(int v) {
     switch (v) {
         case V_PIPE_256_K64_S2: return kTail<256, 256, 64, 2>;
@@ -400,7 +439,7 @@ int choose(const Call& c) {
         if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
     }
     const int v = choose_pipelined(c);
-    if (v != V_GENERIC) return v;
+    if (v != V_GENERIC) return splitk_splits(c) > 1 ? V_SPLITK : v;
     if (repack_ok(c)) return V_REPACK;
     return V_GENERIC;
 }
@@ -601,6 +640,26 @@ void launch_repack_copy(const void* src, long long ld, long long stride, void* d
 // the pipelined kernel on the copies.  Without a workspace (graph capture,
 // allocation failure) the guarded kernel takes the call as it is.
 template <typename T, typename OutT>
+hipError_t launch_splitk(const Call& c, hipStream_t stream) {
+    const int S = splitk_splits(c);
+    float* ws = S > 1 ? stream_workspace((long long)S * c.M * c.N * 4, stream) : nullptr;
+    if (ws == nullptr) return dispatch_typed<T, OutT>(c, choose_pipelined(c), stream);   // e.g. graph capture
+    const Call p = splitk_call(c, S, ws);
+    hipError_t e = dispatch_typed<T, float>(p, choose_pipelined(p), stream);
+    if (e != hipSuccess) return e;
+    bpt::SplitSumArgs a;
+    a.partial = ws;
+    a.C = c.C;
+    a.M = c.M; a.N = c.N; a.ldc = c.ldc;
+    a.splits = S;
+    a.c_vec = aligned16(c.C) && (c.ldc * (long long)sizeof(OutT)) % 16 == 0;
+    const long long threads = c.M * c.N / 8;
+    hipLaunchKernelGGL((bpt::splitk_sum_kernel<OutT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
 hipError_t launch_repack(const Call& c, hipStream_t stream) {
     if (repack_bytes(c) == 0) return dispatch_typed<T, OutT>(c, choose_pipelined(c), stream);   // nothing to copy
     void* ws = stream_workspace(repack_bytes(c), stream);
@@ -628,6 +687,7 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_SKINNY_WIDE: return launch_skinny_wide<T, OutT>(c, stream);
         case V_SKINNY_RING: return launch_skinny_wide<T, OutT, true>(c, stream);
         case V_REPACK: return launch_repack<T, OutT>(c, stream);
+        case V_SPLITK: return launch_splitk<T, OutT>(c, stream);
         case V_BT_256_K32_S4: return launch_pipelined<T, OutT, 256, 256, 32, 4, true>(c, stream);
         case V_BT_128_K32_S4: return launch_pipelined<T, OutT, 128, 128, 32, 4, true>(c, stream);
         case V_BT_GENERIC: return launch_generic<T, OutT, true>(c, stream);
@@ -678,6 +738,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_SKINNY_WIDE: return wide_splits(c) > 0;
         case V_SKINNY_RING: return ring_splits(c) > 0;
         case V_REPACK: return repack_feasible(c);
+        case V_SPLITK: return splitk_splits(c) > 1;
         case V_PIPE_256_K32_S4_AP: return apair_ok(c);
         case V_PERSIST: return persist_ok(c);
         default:

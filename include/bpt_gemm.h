@@ -22,11 +22,15 @@
  *
  * Ownership: A, B and C are DEVICE pointers owned by the caller.  C must not
  * overlap A or B.  The library keeps no per-call state; its one allocation is
- * a workspace used by two paths:
+ * a workspace used by three paths:
  *   - the split-K path for few rows of A (variants
  *     skinny_64x128_ring_k32_s4_splitk and skinny_64x128_w4_k32_s4_splitk
  *     when they split K over workgroups) keeps fp32 partial results there
  *     (at most 256 MiB);
+ *   - the split-K path for few output tiles (variant splitk_pipelined: one
+ *     matrix, more than 128 rows, at most 128 tiles of 128 x 128) keeps the
+ *     fp32 partial products of its 2, 4 or 8 K ranges there (at most
+ *     256 MiB);
  *   - the repack path (variant repack_pipelined: shapes the pipelined kernels
  *     cannot read in place -- K or N not a multiple of 8, leading dimensions,
  *     batch strides or bases not 16-byte granular -- with at least 2^24
@@ -38,8 +42,8 @@
  * freed before the process exits.  Calls on one stream use it in stream
  * order; calls on different streams never share one.  A call made while its
  * stream is being captured into a graph, or one whose allocation fails,
- * takes a path without workspace (the skinny kernel unsplit, the guarded
- * kernel instead of the repack) -- so a captured graph never refers to a
+ * takes a path without workspace (the skinny or pipelined kernel unsplit,
+ * the guarded kernel instead of the repack) -- so a captured graph never refers to a
  * library buffer.
  *
  * Execution: the call validates its arguments on the host, enqueues the

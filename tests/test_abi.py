@@ -184,8 +184,9 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 128, 8192, 8192, 8192, 8192) == ring
     assert pkg.select_variant("f16", 1, 96, 8192, 8192, 8192, 8192) == ring
     assert pkg.select_variant("f16", 1, 128, 4096, 4096, 4096, 4096) == ring
-    assert pkg.select_variant("f16", 1, 129, 8192, 8192, 8192, 8192) == v["pipelined_128x128x32_s4"]
-    assert pkg.select_variant("f16", 1, 192, 8192, 8192, 8192, 8192) == v["pipelined_128x128x32_s4"]
+    splitk = v["splitk_pipelined"]
+    assert pkg.select_variant("f16", 1, 129, 8192, 8192, 8192, 8192) == splitk
+    assert pkg.select_variant("f16", 1, 192, 8192, 8192, 8192, 8192) == splitk
     assert pkg.select_variant("f16", 1, 128, 32768, 4096, 4096, 32768) == v["pipelined_256x256x32_s4_apair"]
     # ... which makes the other two skinny kernels forced-only: each needs
     # K a multiple of 256 or more, where the ring fits at least as many
@@ -197,6 +198,16 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 4096, 4092, 4096, 4096, 4092) == repack
     # ... unless K is too short for any ring even after padding
     assert pkg.select_variant("f16", 1, 4096, 4092, 96, 96, 4092) == v["generic_64x64x16"]
+    # split-K: at most 128 tiles of 128 x 128 leave half the CUs idle, so K
+    # is split over the pipelined kernel's batch (2, 4 or 8 ranges, each a
+    # multiple of 64 and at least 256 long, tiles x splits <= 256)
+    assert pkg.select_variant("f16", 1, 256, 8192, 8192, 8192, 8192) == splitk    # 128 tiles x 2
+    assert pkg.select_variant("f16", 1, 1024, 1024, 8192, 8192, 1024) == splitk   # 64 tiles x 4
+    assert pkg.select_variant("bf16", 1, 512, 512, 4096, 4096, 512, True) == splitk  # 16 tiles x 8
+    assert pkg.select_variant("f16", 1, 384, 8192, 8192, 8192, 8192) == v["pipelined_128x128x32_s4"]  # 192 tiles
+    assert pkg.select_variant("f16", 1, 256, 8192, 384, 384, 8192) == v["pipelined_128x128x32_s4"]    # K/2 < 256
+    assert pkg.select_variant("f16", 2, 256, 8192, 8192, 8192, 8192) not in (splitk, 0)                # batched
+    assert pkg.select_variant("f16", 1, 256, 8192, 8200, 8200, 8192) != splitk    # K not a multiple of 128
     # rejected / nothing to do
     assert pkg.select_variant("f16", 1, 0, 256, 256, 256, 256) == 0
     assert pkg.select_variant("f16", 1, 16, 16, 16, 8, 16) == 0

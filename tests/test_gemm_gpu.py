@@ -299,14 +299,15 @@ def test_repeat_runs_bitwise_identical():
         assert torch.equal(o, outs[0])
 
 
-def test_graph_capture_of_a_split_k_call():
+@pytest.mark.parametrize("M,N,K,vname", [(64, 2048, 4096, "skinny_64x128_ring_k32_s4_splitk"),   # 8 splits eager
+                                         (256, 2048, 4096, "splitk_pipelined")])                # 8 splits eager
+def test_graph_capture_of_a_split_k_call(M, N, K, vname):
     """A call captured into a graph must not use the per-stream workspace (a
-    graph would keep its address): captured, the split-K skinny path runs
-    unsplit.  Exact-integer inputs make the split (eager) and unsplit
-    (captured) sums bit-identical, so every replay -- with eager calls and
-    synchronisations between replays -- must equal the oracle exactly."""
-    M, N, K = 64, 2048, 4096                      # shared-ring skinny kernel, 8 splits when eager
-    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["skinny_64x128_ring_k32_s4_splitk"]
+    graph would keep its address): captured, the split-K paths run unsplit.
+    Exact-integer inputs make the split (eager) and unsplit (captured) sums
+    bit-identical, so every replay -- with eager calls and synchronisations
+    between replays -- must equal the oracle exactly."""
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()[vname]
     A = inputs.small_integers((M, K), 7501)
     B = inputs.small_integers((K, N), 7502)
     ref = torch.from_numpy(oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"))
@@ -476,6 +477,79 @@ def test_split_k_repeated_and_interleaved(vname):
             assert torch.equal(C.cpu(), lone), (M, N, K, rep)
         for C in rps:
             assert torch.equal(C.cpu(), rp_ref)
+
+
+# split-K over the pipelined kernel's batch: M > 128, at most 128 tiles of
+# 128 x 128, K a multiple of 64 * S with K / S >= 256.  Ragged M and N;
+# S = 4, 8, 2, 8, 2 and 4 below
+SHAPES_SPLITK = [(256, 1024, 1024), (300, 520, 2048), (129, 136, 512), (640, 768, 4096), (200, 8192, 1024),
+                 (1024, 1024, 8192)]
+
+
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True), ("bf16", False)])
+def test_splitk_parity(dtype, out_fp32):
+    """Random inputs within tolerance, integer inputs bitwise (the partials
+    and their sum are exact), each through the automatic choice."""
+    v = pkg.variants()["splitk_pipelined"]
+    for i, (M, N, K) in enumerate(SHAPES_SPLITK):
+        say(f"[split-K] M={M} N={N} K={K} {dtype} out_fp32={out_fp32}")
+        assert pkg.select_variant(dtype, 1, M, N, K, K, N, out_fp32) == v
+        A = inputs.uniform((M, K), 7901 + i, nonzero=True, dtype=dtype)
+        B = inputs.uniform((K, N), 7911 + i, nonzero=True, dtype=dtype)
+        check_random(A, B, dtype, out_fp32)
+        A = inputs.small_integers((M, K), 7921 + i, dtype=dtype)
+        B = inputs.small_integers((K, N), 7931 + i, dtype=dtype)
+        check_exact(A, B, dtype, out_fp32)
+
+
+@pytest.mark.parametrize("out_fp32", [False, True])
+def test_splitk_padded_views(out_fp32):
+    """Views with padded leading dimensions; C rows of odd length (element
+    stores from the sum kernel).  The padding, NaN, stays untouched."""
+    M, N, K = 300, 520, 2048
+    A0 = inputs.small_integers((M, K + 64), 7941)
+    B0 = inputs.small_integers((K, N + 8), 7942)
+    A, B = A0[:, :K], B0[:, :N]
+    ref = oracle.gemm(inputs.bits(A.contiguous()), inputs.bits(B.contiguous()), "f16")
+    out_t = torch.float32 if out_fp32 else torch.float16
+    Cbuf = torch.full((M, N + 3), float("nan"), dtype=out_t, device=DEV)
+    C = Cbuf[:, :N]
+    Ad, Bd = A0.to(DEV)[:, :K], B0.to(DEV)[:, :N]
+    assert pkg.select_variant("f16", 1, M, N, K, K + 64, N + 8, out_fp32) == pkg.variants()["splitk_pipelined"]
+    pkg.gemm_ex(Ad, Bd, C, out_fp32=out_fp32)
+    torch.cuda.synchronize()
+    got = C.cpu()
+    if out_fp32:
+        assert np.array_equal(got.numpy(), ref)
+    else:
+        assert np.array_equal(as_bits(got), oracle.encode(ref, "f16"))
+    assert torch.isnan(Cbuf[:, N:].float()).all()
+
+
+def test_splitk_repeated_with_other_workspace_users():
+    """Split-K calls of different split counts in a row on one stream, with
+    skinny split-K calls (the same workspace) in between: each equals the
+    lone call bit for bit."""
+    v = pkg.variants()["splitk_pipelined"]
+    shapes = [(256, 1024, 1024), (200, 8192, 1024), (640, 768, 4096)]
+    sk_A = inputs.uniform((64, 4096), 7951, nonzero=True).to(DEV)
+    sk_B = inputs.uniform((4096, 2048), 7952, nonzero=True).to(DEV)
+    sk_ref = pkg.gemm_ex(sk_A, sk_B, out_fp32=True).cpu()
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A = inputs.uniform((M, K), 7961 + i, nonzero=True)
+        B = inputs.uniform((K, N), 7971 + i, nonzero=True)
+        data.append((A.to(DEV), B.to(DEV), run(A, B, "f16", True, v)))
+    outs, sks = [], []
+    for rep in range(4):
+        for i, (Ad, Bd, _) in enumerate(data):
+            outs.append((i, pkg.gemm_ex(Ad, Bd, out_fp32=True, variant=v)))
+            sks.append(pkg.gemm_ex(sk_A, sk_B, out_fp32=True))
+    torch.cuda.synchronize()
+    for i, C in outs:
+        assert torch.equal(C.cpu(), data[i][2]), i
+    for C in sks:
+        assert torch.equal(C.cpu(), sk_ref)
 
 
 # ----------------------------------------------------------------------------
