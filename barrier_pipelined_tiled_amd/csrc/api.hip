@@ -378,13 +378,14 @@ bool repack_ok(const Call& c) {
 // entry) into fp32 partials in the stream's workspace, and splitk_sum_kernel
 // adds them in split order.  S is the largest power of two (at most 8) that
 // keeps the tiles within one workgroup per CU, with K/S a multiple of 64 and
-// at least 256.
+// at least 256.  With B given transposed, entry s reads Bt from column
+// s*K/S (batch stride K/S).
 Call splitk_call(const Call& c, int S, void* ws) {
     Call p = c;
     p.batch = S;
     p.K = c.K / S;
     p.sA = p.K;
-    p.sB = p.K * c.ldb;
+    p.sB = c.bt ? p.K : p.K * c.ldb;
     p.C = ws;
     p.ldc = c.N;
     p.sC = c.M * c.N;
@@ -392,8 +393,12 @@ Call splitk_call(const Call& c, int S, void* ws) {
     return p;
 }
 
+// the pipelined variant for a call in either layout (the plain one when none)
+int choose_layout(const Call& c) { return c.bt ? choose_bt(c) : choose_pipelined(c); }
+bool is_generic(int v) { return v == V_GENERIC || v == V_BT_GENERIC; }
+
 int splitk_splits(const Call& c) {
-    if (c.bt || c.batch != 1 || c.M <= 128 || c.K <= 0 || c.N % 8 != 0) return 0;
+    if (c.batch != 1 || c.M <= 128 || c.K <= 0 || c.N % 8 != 0) return 0;
     const long long tiles = ((c.M + 127) / 128) * ((c.N + 127) / 128);
     alignas(256) static char probe[256];           // stands in for the workspace
     int best = 0;
@@ -401,7 +406,7 @@ int splitk_splits(const Call& c) {
         if (tiles * S > 256) break;
         if (c.K % (64LL * S) != 0 || c.K / S < 256) break;
         if ((long long)S * c.M * c.N * 4 > kWorkspaceMax) break;
-        if (choose_pipelined(splitk_call(c, S, probe)) == V_GENERIC) break;
+        if (is_generic(choose_layout(splitk_call(c, S, probe)))) break;
         best = S;
     }
     return best;
@@ -419,7 +424,10 @@ bool variant_tail(int v) {
 }
 
 int choose(const Call& c) {
-    if (c.bt) return choose_bt(c);
+    if (c.bt) {
+        const int v = choose_bt(c);
+        return v != V_BT_GENERIC && splitk_splits(c) > 1 ? V_SPLITK : v;
+    }
     // few rows of A: stream B once with a skinny kernel when that yields at
     // least half a workgroup per CU; the 128-column ones read B in 256-byte
     // row pieces, which stream faster than the narrow one's 64-byte pieces,
@@ -643,9 +651,9 @@ template <typename T, typename OutT>
 hipError_t launch_splitk(const Call& c, hipStream_t stream) {
     const int S = splitk_splits(c);
     float* ws = S > 1 ? stream_workspace((long long)S * c.M * c.N * 4, stream) : nullptr;
-    if (ws == nullptr) return dispatch_typed<T, OutT>(c, choose_pipelined(c), stream);   // e.g. graph capture
+    if (ws == nullptr) return dispatch_typed<T, OutT>(c, choose_layout(c), stream);   // e.g. graph capture
     const Call p = splitk_call(c, S, ws);
-    hipError_t e = dispatch_typed<T, float>(p, choose_pipelined(p), stream);
+    hipError_t e = dispatch_typed<T, float>(p, choose_layout(p), stream);
     if (e != hipSuccess) return e;
     bpt::SplitSumArgs a;
     a.partial = ws;
@@ -726,7 +734,8 @@ bpt_status validate(const Call& c) {
 }
 
 bool variant_accepts(const Call& c, int v) {
-    if (is_bt_variant(v) != (c.bt != 0)) return false;       // each layout has its own variants
+    // each layout has its own variants; split-K runs either layout's
+    if (v != V_SPLITK && is_bt_variant(v) != (c.bt != 0)) return false;
     switch (v) {
         case V_BT_256_K32_S4: return pipelined_bt_ok(c, 32, 4, kTailBt<256, 256, 32, 4>);
         case V_BT_128_K32_S4: return pipelined_bt_ok(c, 32, 4, kTailBt<128, 128, 32, 4>);

@@ -28,7 +28,8 @@
  *     when they split K over workgroups) keeps fp32 partial results there
  *     (at most 256 MiB);
  *   - the split-K path for few output tiles (variant splitk_pipelined: one
- *     matrix, more than 128 rows, at most 128 tiles of 128 x 128) keeps the
+ *     matrix, more than 128 rows, at most 128 tiles of 128 x 128, N a
+ *     multiple of 8, B in either layout) keeps the
  *     fp32 partial products of its 2, 4 or 8 K ranges there (at most
  *     256 MiB);
  *   - the repack path (variant repack_pipelined: shapes the pipelined kernels

@@ -239,6 +239,9 @@ def test_bt_layout_entry_point(L):
     assert pkg.select_variant("f16", 1, 256, 200, 256, 256, 256, bt=True) == v["pipelined_bt_128x128x32_s4"]
     # odd K and odd leading dimensions: the guarded kernel
     assert pkg.select_variant("f16", 1, 300, 201, 250, 250, 250, bt=True) == v["generic_bt_64x64x16"]
+    # few output tiles: split-K, as for the other layout (N a multiple of 8)
+    assert pkg.select_variant("f16", 1, 256, 8192, 8192, 8192, 8192, bt=True) == v["splitk_pipelined"]
+    assert pkg.select_variant("f16", 1, 256, 8190, 8192, 8192, 8192, bt=True) == v["pipelined_bt_128x128x32_s4"]
 
 
 

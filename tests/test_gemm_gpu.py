@@ -502,6 +502,32 @@ def test_splitk_parity(dtype, out_fp32):
         check_exact(A, B, dtype, out_fp32)
 
 
+@pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("bf16", True)])
+def test_splitk_bt_parity(dtype, out_fp32):
+    """B given transposed (N x K): each K range reads its columns of Bt.
+    Random inputs within tolerance, integer inputs bitwise."""
+    v = pkg.variants()["splitk_pipelined"]
+    for i, (M, N, K) in enumerate(SHAPES_SPLITK[:4]):
+        say(f"[split-K bt] M={M} N={N} K={K} {dtype} out_fp32={out_fp32}")
+        assert pkg.select_variant(dtype, 1, M, N, K, K, K, out_fp32, bt=True) == v
+        for kind in ("random", "exact"):
+            if kind == "random":
+                A = inputs.uniform((M, K), 7981 + i, nonzero=True, dtype=dtype)
+                Bt = inputs.uniform((N, K), 7991 + i, nonzero=True, dtype=dtype)
+            else:
+                A = inputs.small_integers((M, K), 7985 + i, dtype=dtype)
+                Bt = inputs.small_integers((N, K), 7995 + i, dtype=dtype)
+            got = pkg.gemm_ex_bt(A.to(DEV), Bt.to(DEV), dtype=dtype, out_fp32=out_fp32).cpu()
+            ref = oracle.gemm(inputs.bits(A), inputs.bits(Bt.t().contiguous()), dtype)
+            if kind == "random":
+                m = oracle.compare(got.float().numpy(), ref, K)
+                assert m["ok"], m
+            elif out_fp32:
+                assert np.array_equal(got.numpy(), ref)
+            else:
+                assert np.array_equal(as_bits(got), oracle.encode(ref, dtype))
+
+
 @pytest.mark.parametrize("out_fp32", [False, True])
 def test_splitk_padded_views(out_fp32):
     """Views with padded leading dimensions; C rows of odd length (element
