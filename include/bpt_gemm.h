@@ -128,9 +128,10 @@ bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
  * variant: 0 chooses automatically among the variants named
  * "pipelined_bt_*" and "generic_bt_*" (fast path: A and Bt 16-byte aligned,
  * lda, ldbt and the batch strides multiples of 8, K >= 128 and either a
- * multiple of 32 or of 8 with a tail; any N), which are the only ones this
- * entry point takes; the others are for gemm_ex and are rejected here with
- * BPT_ERR_UNSUPPORTED, and vice versa. */
+ * multiple of 32 or of 8 with a tail; any N) and "splitk_pipelined", which
+ * are the only ones this entry point takes; the others are for gemm_ex and
+ * are rejected here with BPT_ERR_UNSUPPORTED, and vice versa
+ * ("splitk_pipelined" serves both). */
 bpt_status gemm_ex_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                       const void *A, int64_t lda, int64_t strideA,
                       const void *Bt, int64_t ldbt, int64_t strideBt,
