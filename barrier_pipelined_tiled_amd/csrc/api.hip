@@ -433,18 +433,26 @@ int choose(const Call& c) {
     // row pieces, which stream faster than the narrow one's 64-byte pieces,
     // and the shared-ring one of them streams fastest and takes any K that
     // is a multiple of 32
-    if (c.M <= 64) {
+    if (c.M <= 128) {
         const int S = ring_splits(c);
-        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
-        if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
-    } else if (c.M <= 128 && (c.N + 127) / 128 * c.batch < 256) {
-        // two row blocks of the ring kernel (B streamed once per block) beat
-        // 128 x 128 tiles that give fewer than one workgroup per CU: 128 x
-        // 8192^2 0.0627 -> 0.0393 ms, 96 x 8192^2 0.0539 -> 0.0371, 128 x
-        // 4096^2 0.0315 -> 0.0152 on one machine; at 192 and 256 rows the
-        // two were even
-        const int S = ring_splits(c);
-        if (S > 0 && wide_blocks_per_launch(c) * S >= 128) return V_SKINNY_RING;
+        const long long ring_wgs = S > 0 ? wide_blocks_per_launch(c) * S : 0;
+        const long long tiles128 = (c.M + 127) / 128 * ((c.N + 127) / 128) * c.batch;
+        if (c.M <= 64) {
+            if (ring_wgs >= 128) return V_SKINNY_RING;
+            if ((c.N + 31) / 32 * c.batch >= 128 && skinny_ok(c)) return V_SKINNY;
+        } else if (tiles128 < 256 && ring_wgs >= 128) {
+            // two row blocks of the ring kernel (B streamed once per block)
+            // beat 128 x 128 tiles that give fewer than one workgroup per
+            // CU: 128 x 8192^2 0.0627 -> 0.0393 ms, 96 x 8192^2 0.0539 ->
+            // 0.0371, 128 x 4096^2 0.0315 -> 0.0152 on one machine; at 192
+            // and 256 rows the two were even
+            return V_SKINNY_RING;
+        }
+        // narrow outputs over long K: too few workgroups either way, but the
+        // ring's K splits give more of them than the output tiles do (64 x
+        // 512 x 65536: 32 against 4, 0.354 -> 0.058 ms; 64 x 256 x 8192
+        // 0.0464 -> 0.0123 ms)
+        if (tiles128 < 256 && ring_wgs > tiles128) return V_SKINNY_RING;
     }
     const int v = choose_pipelined(c);
     if (v != V_GENERIC) return splitk_splits(c) > 1 ? V_SPLITK : v;

@@ -179,6 +179,12 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 64, 4096, 1024, 1024, 4096) == ring     # 32 blocks x 8 splits
     assert pkg.select_variant("f16", 1, 64, 8192, 768, 768, 8192) == ring       # 64 blocks x 4 splits
     assert pkg.select_variant("f16", 1, 64, 16384, 96, 96, 16384) == ring       # 3 chunks, no split
+    # narrow outputs over long K: fewer than 128 workgroups either way, but
+    # the ring's K splits give more than the output tiles
+    assert pkg.select_variant("f16", 1, 64, 512, 65536, 65536, 512) == ring      # 4 blocks x 8 against 4 tiles
+    assert pkg.select_variant("f16", 1, 64, 256, 8192, 8192, 256) == ring        # 2 x 8 against 2
+    # ... but not when the output tiles already fill the chip
+    assert pkg.select_variant("f16", 64, 100, 4096, 256, 256, 4096) != ring
     # up to 128 rows (two row blocks) while 128 x 128 tiles would leave CUs
     # idle; from 129 rows, or with 256 or more such tiles, the pipelined kernels
     assert pkg.select_variant("f16", 1, 128, 8192, 8192, 8192, 8192) == ring

@@ -652,11 +652,13 @@ def test_full_size_exact_integers(name):
         assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (96, 8192, 2048), (65, 1000, 1024)])
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (96, 8192, 2048), (65, 1000, 1024), (64, 512, 65536),
+                                   (64, 256, 8192)])
 def test_mid_rows_take_the_ring_kernel_exactly(M, N, K):
-    """65 to 128 rows with few 128 x 128 tiles: the automatic choice runs the
-    shared-ring skinny kernel over two row blocks (the second ragged below
-    128 rows), split over K.  Integer inputs: equal to the oracle bitwise."""
+    """65 to 128 rows with few 128 x 128 tiles, or narrow outputs over long K:
+    the automatic choice runs the shared-ring skinny kernel (two row blocks,
+    the second ragged below 128 rows, for the former), split over K.
+    Integer inputs: equal to the oracle bitwise."""
     say(f"[mid rows] M={M} N={N} K={K}")
     assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()["skinny_64x128_ring_k32_s4_splitk"]
     A = inputs.small_integers((M, K), 8301 + M)
