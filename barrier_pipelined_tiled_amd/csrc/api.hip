@@ -189,7 +189,7 @@ int skinny_splits(const Call& c, bool (*fits)(const Call&, int), long long targe
     if (c.K <= 0 || !skinny_operands_ok(c) || !fits(c, 1)) return 0;
     const long long blocks = wide_blocks_per_launch(c);
     int best = 1;
-    for (int S = 2; S <= 8; S *= 2) {
+    for (int S = 2; S <= 64; S *= 2) {
         if (!fits(c, S)) break;
         if (blocks * S * 64 * kSwBN * 4 > kWorkspaceMax) break;
         if (blocks * best >= target) break;
@@ -402,7 +402,7 @@ int splitk_splits(const Call& c) {
     const long long tiles = ((c.M + 127) / 128) * ((c.N + 127) / 128);
     alignas(256) static char probe[256];           // stands in for the workspace
     int best = 0;
-    for (int S = 2; S <= 8; S *= 2) {
+    for (int S = 2; S <= 64; S *= 2) {
         if (tiles * S > 256) break;
         if (c.K % (64LL * S) != 0 || c.K / S < 256) break;
         if ((long long)S * c.M * c.N * 4 > kWorkspaceMax) break;
@@ -556,7 +556,10 @@ void launch_split_sum(const bpt::SkinnySumArgs& a, int S, hipStream_t stream) {
     const dim3 grid((unsigned)((threads + 255) / 256));
     if (S == 2) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 2, OutT>), grid, dim3(256), 0, stream, a);
     else if (S == 4) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 4, OutT>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 8, OutT>), grid, dim3(256), 0, stream, a);
+    else if (S == 8) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 8, OutT>), grid, dim3(256), 0, stream, a);
+    else if (S == 16) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 16, OutT>), grid, dim3(256), 0, stream, a);
+    else if (S == 32) hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 32, OutT>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((bpt::skinny_sum_kernel<kSwBN, 64, OutT>), grid, dim3(256), 0, stream, a);
 }
 
 template <typename T, typename OutT, bool RING = false>

@@ -562,17 +562,43 @@ __global__ __launch_bounds__(256) void skinny_sum_kernel(SkinnySumArgs args) {
     if (blk >= args.blocks) return;
     const int e = (int)(gid - blk * (BLOCK / 8)) * 8;
     const float* p = args.partial + blk * S * BLOCK + e;
-    float4_t v[S][2];
+    float4_t lo, hi;
+    if constexpr (S <= 8) {
+        float4_t v[S][2];
 #pragma unroll
-    for (int q = 0; q < S; ++q) {
-        v[q][0] = *(const float4_t*)(p + q * BLOCK);
-        v[q][1] = *(const float4_t*)(p + q * BLOCK + 4);
-    }
-    float4_t lo = v[0][0], hi = v[0][1];
+        for (int q = 0; q < S; ++q) {
+            v[q][0] = *(const float4_t*)(p + q * BLOCK);
+            v[q][1] = *(const float4_t*)(p + q * BLOCK + 4);
+        }
+        lo = v[0][0];
+        hi = v[0][1];
 #pragma unroll
-    for (int q = 1; q < S; ++q) {
-        lo += v[q][0];
-        hi += v[q][1];
+        for (int q = 1; q < S; ++q) {
+            lo += v[q][0];
+            hi += v[q][1];
+        }
+    } else {
+        // more splits than registers for all of them: groups of 8 loads,
+        // still added in split order
+#pragma unroll
+        for (int g = 0; g < S; g += 8) {
+            float4_t v[8][2];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                v[q][0] = *(const float4_t*)(p + (g + q) * BLOCK);
+                v[q][1] = *(const float4_t*)(p + (g + q) * BLOCK + 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (g + q == 0) {
+                    lo = v[q][0];
+                    hi = v[q][1];
+                } else {
+                    lo += v[q][0];
+                    hi += v[q][1];
+                }
+            }
+        }
     }
     const int tn = (int)(blk % args.tiles_n);
     const long long rest = blk / args.tiles_n;

@@ -481,9 +481,9 @@ def test_split_k_repeated_and_interleaved(vname):
 
 # split-K over the pipelined kernel's batch: M > 128, at most 128 tiles of
 # 128 x 128, K a multiple of 64 * S with K / S >= 256.  Ragged M and N;
-# S = 4, 8, 2, 8, 2 and 4 below
+# S = 4, 8, 2, 8, 2, 4 and 32 below
 SHAPES_SPLITK = [(256, 1024, 1024), (300, 520, 2048), (129, 136, 512), (640, 768, 4096), (200, 8192, 1024),
-                 (1024, 1024, 8192)]
+                 (1024, 1024, 8192), (256, 512, 32768)]
 
 
 @pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True), ("bf16", False)])
