@@ -376,7 +376,7 @@ bool repack_ok(const Call& c) {
 // a workgroup) is computed as S K-ranges at once: the pipelined kernel runs
 // with the ranges as its batch (A advanced by K/S columns, B by K/S rows per
 // entry) into fp32 partials in the stream's workspace, and splitk_sum_kernel
-// adds them in split order.  S is the largest power of two (at most 8) that
+// adds them in split order.  S is the largest power of two (at most 64) that
 // keeps the tiles within one workgroup per CU, with K/S a multiple of 64 and
 // at least 256.  With B given transposed, entry s reads Bt from column
 // s*K/S (batch stride K/S).

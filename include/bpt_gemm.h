@@ -30,7 +30,7 @@
  *   - the split-K path for few output tiles (variant splitk_pipelined: one
  *     matrix, more than 128 rows, at most 128 tiles of 128 x 128, N a
  *     multiple of 8, B in either layout) keeps the
- *     fp32 partial products of its 2, 4 or 8 K ranges there (at most
+ *     fp32 partial products of its 2 to 64 K ranges there (at most
  *     256 MiB);
  *   - the repack path (variant repack_pipelined: shapes the pipelined kernels
  *     cannot read in place -- K or N not a multiple of 8, leading dimensions,

@@ -169,7 +169,7 @@ def test_automatic_variant_choice():
     # (four stages need four)
     assert pkg.select_variant("f16", 1, 256, 256, 64, 64, 256) == v["generic_64x64x16"]
     # few rows of A: the shared-ring skinny kernel (128-column blocks, K
-    # split over up to 8 workgroups to reach one workgroup per CU), for any K
+    # split over up to 64 workgroups to reach one workgroup per CU), for any K
     # that is a multiple of 32 ...
     ring = v["skinny_64x128_ring_k32_s4_splitk"]
     wide, narrow = v["skinny_64x128_w4_k32_s4_splitk"], v["skinny_64x32_w4_k64_s4"]
@@ -205,7 +205,7 @@ def test_automatic_variant_choice():
     # ... unless K is too short for any ring even after padding
     assert pkg.select_variant("f16", 1, 4096, 4092, 96, 96, 4092) == v["generic_64x64x16"]
     # split-K: at most 128 tiles of 128 x 128 leave half the CUs idle, so K
-    # is split over the pipelined kernel's batch (2, 4 or 8 ranges, each a
+    # is split over the pipelined kernel's batch (2 to 64 ranges, each a
     # multiple of 64 and at least 256 long, tiles x splits <= 256)
     assert pkg.select_variant("f16", 1, 256, 8192, 8192, 8192, 8192) == splitk    # 128 tiles x 2
     assert pkg.select_variant("f16", 1, 1024, 1024, 8192, 8192, 1024) == splitk   # 64 tiles x 4
