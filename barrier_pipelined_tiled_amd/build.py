@@ -2,9 +2,13 @@
 
 The library is one translation unit, ``csrc/api.hip``, which includes the
 kernel headers.  Packed-fp32 VALU forms are disabled for all device code.
+The same compilation keeps its gfx950 assembly (-save-temps, in ``_build/``)
+and writes ``libbpt_gemm.kernels.json`` beside the library: every kernel's
+resource use and a hash of its machine code (asm_info).
 """
 from __future__ import annotations
 
+import json
 import os
 import shutil
 import subprocess
@@ -15,6 +19,9 @@ SRC = os.path.join(CSRC, "api.hip")
 LIB_NAME = "libbpt_gemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+ASM_PATH = os.path.join(BUILD_DIR, f"api-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+KERNELS_JSON = os.path.join(PKG_DIR, "libbpt_gemm.kernels.json")
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
@@ -32,14 +39,34 @@ def hipcc() -> str:
 
 
 def build(out: str = LIB_PATH, extra: list[str] | None = None) -> str:
-    """Compile the library; returns the path of the shared object."""
+    """Compile the library; returns the path of the shared object.  Also
+    keeps the device assembly and writes the kernel table (kernel_table)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-o", tmp, SRC]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    cmd = [hipcc(), *HIPCC_FLAGS, "-save-temps", *(extra or []), "-o", tmp, SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD_DIR)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr[-6000:]}")
     os.replace(tmp, out)
+    if out == LIB_PATH:
+        write_kernel_table()
     return out
+
+
+def write_kernel_table(asm_path: str = ASM_PATH, path: str = KERNELS_JSON) -> dict:
+    """name -> {"code": hash of the kernel's machine code, resource use} for
+    every kernel of the library, from the kept assembly."""
+    try:
+        from . import asm_info
+    except ImportError:                # run as a script
+        import asm_info
+    with open(asm_path) as f:
+        ks = asm_info.kernels(f.read())
+    table = {n: dict(code=asm_info.code_hash(k), **k["meta"]) for n, k in sorted(ks.items())}
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    return table
 
 
 CALIB_SRC = os.path.join(CSRC, "calib.hip")
@@ -58,7 +85,8 @@ def build_calib(out: str = CALIB_PATH) -> str:
 
 
 def device_asm(out_dir: str) -> str:
-    """Emit the gfx950 assembly of the library into out_dir; returns the .s path."""
+    """Emit the gfx950 assembly of the library into out_dir (a compilation of
+    its own; build() keeps the same text in ASM_PATH); returns the .s path."""
     os.makedirs(out_dir, exist_ok=True)
     s_path = os.path.join(out_dir, "api-gfx950.s")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20",

@@ -9,9 +9,11 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/bpt_gemm.h"
 #include "attention.hpp"
@@ -103,6 +105,9 @@ struct Call {
     int out_fp32;
     long long nb = 0;       // columns of B when it is a padded copy (0: N)
     int bt = 0;             // 1: B is given transposed, N x K with ldb >= K
+    void* ws = nullptr;     // workspace granted to the call (nullptr: none; the
+                            // split paths then run unsplit, the repack route
+                            // falls back to the guarded kernel)
 };
 
 constexpr long long kI31 = (1LL << 31) - 1;
@@ -160,7 +165,7 @@ bool skinny_ok(const Call& c) {
 // 32-deep chunks, 4 B stages and 2 A slots per wave, K split over `splits`
 // workgroups per block
 constexpr int kSwWaves = 4, kSwChunk = 32, kSwStages = 4, kSwSlots = 2, kSwBN = 128;
-constexpr long long kWorkspaceMax = 256LL << 20;   // bytes per (device, stream)
+constexpr long long kWorkspaceMax = 256LL << 20;   // bytes of split partials per call
 
 long long wide_blocks_per_launch(const Call& c) {
     long long nb = c.batch < 65535 ? c.batch : 65535;
@@ -201,40 +206,200 @@ int skinny_splits(const Call& c, bool (*fits)(const Call&, int), long long targe
 int wide_splits(const Call& c) { return skinny_splits(c, wide_split_fits); }
 int ring_splits(const Call& c) { return skinny_splits(c, ring_split_fits); }
 
-// One device workspace per (device, stream), grown on demand.  A grown-out
-// buffer is kept, not freed, until the process ends: a call on another host
-// thread may still hold its address, and nothing here can tell when that
-// call's kernels are done with it (the waste stays below the final size,
-// since each buffer is at least twice the one before).  nullptr when no
-// workspace may be used: the allocation fails, or the stream is being
-// captured into a graph -- a graph must not hold the address of a buffer
-// that a later call could outgrow, so captured calls run unsplit.
-float* stream_workspace(long long bytes, hipStream_t stream) {
+// ---- workspace ----------------------------------------------------------------
+// The fp32 partials of the split-K paths and the padded copies of the repack
+// route live in device buffers from a pool per device.  Each buffer carries
+// an event recorded on the caller's stream after the last kernel that used
+// it, and a call that takes a buffer whose event has not completed makes its
+// stream wait for that event first (hipStreamWaitEvent).  So calls on
+// different streams -- hipStreamPerThread from several host threads, a new
+// stream that received a destroyed one's handle while its kernels still ran
+// -- never use a buffer at the same time, whatever their handles.
+//
+// A buffer is allocated when no pooled one is free and large enough (the
+// first such call on the device, a call needing more than before, or calls
+// in flight on more streams than the pool holds).  A grown-out buffer is
+// kept, not freed, until the process ends: hipFree synchronises the device.
+// Per device: at most kPoolSlots buffers (more only while more host threads
+// are between taking and returning one), each at most the largest single
+// request (split partials <= 256 MiB, repack copies <= 1 GiB), plus the
+// grown-out ones, whose total stays below the final sizes (each replacement
+// is at least twice the size it replaces).  A call made while its stream is
+// being captured into a graph gets no buffer (a graph must not hold the
+// address of a buffer a later call could outgrow) and runs its kernel
+// unsplit, or the guarded kernel instead of the repack.
+constexpr int kPoolSlots = 4;
+
+struct WsSlot {
+    void* ptr = nullptr;
+    long long bytes = 0;
+    hipEvent_t done = nullptr;       // recorded after the last kernel that used ptr
+    hipStream_t last = nullptr;      // the stream handle it was recorded on
+    bool recorded = false;
+    bool busy = false;               // taken by a call that has not yet recorded `done`
+};
+
+struct WsPool {
+    std::mutex mu;
+    std::vector<std::unique_ptr<WsSlot>> slots;
+    long long retired_bytes = 0;     // grown-out buffers, kept until exit
+};
+
+WsPool& pool_of(int dev) {
     static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, std::pair<void*, long long>> spaces;
+    static std::map<int, std::unique_ptr<WsPool>> pools;
+    std::lock_guard<std::mutex> lock(mu);
+    auto& p = pools[dev];
+    if (!p) p = std::make_unique<WsPool>();
+    return *p;
+}
+
+}  // namespace
+
+// Which pooled buffer a call takes (the pure policy; no HIP calls).  For
+// slot i: bytes[i], busy[i] (0/1: taken by a call in progress), state[i] (0:
+// never used, 1: its last use has completed, 2: its last use may still
+// run), same[i] (1: that last use was recorded on the caller's stream
+// handle).  Returns the slot to take, or n for a new buffer; *wait = 1 when
+// the caller's stream must first wait for the slot's last use (every slot
+// in state 2, the caller's own handle included), *grow = 1 when the slot is
+// too small and gets a new buffer (the old one is kept and not waited for).
+// Preference: an idle buffer; one last used on the caller's handle (a wait
+// within one stream); a new buffer while the pool has fewer than `cap`;
+// one busy with another stream's work (the wait orders the two); growing an
+// idle-sized one; a new buffer beyond `cap`.
+extern "C" int bpt_ws_choose(int n, const long long* bytes, const int* busy, const int* state, const int* same,
+                             long long need, int cap, int* wait, int* grow) {
+    *wait = 0;
+    *grow = 0;
+    for (int i = 0; i < n; ++i)
+        if (!busy[i] && bytes[i] >= need && state[i] != 2) return i;
+    for (int i = 0; i < n; ++i)
+        if (!busy[i] && bytes[i] >= need && same[i]) {
+            *wait = 1;
+            return i;
+        }
+    if (n < cap) return n;
+    for (int i = 0; i < n; ++i)
+        if (!busy[i] && bytes[i] >= need) {
+            *wait = 1;
+            return i;
+        }
+    for (int i = 0; i < n; ++i)
+        if (!busy[i]) {
+            *grow = 1;
+            return i;
+        }
+    return n;
+}
+
+namespace {
+
+// A pooled buffer taken by one call: ptr is nullptr when the call gets none.
+struct WsLease {
+    WsPool* pool = nullptr;
+    WsSlot* slot = nullptr;
+    void* ptr = nullptr;
+};
+
+long long ws_size_for(long long need, long long old) {
+    long long want = 1LL << 20;
+    while (want < need) want *= 2;
+    if (want < 2 * old) want = 2 * old;
+    if (want > (1LL << 30)) want = need > (1LL << 30) ? need : (1LL << 30);
+    return want;
+}
+
+WsLease ws_acquire(long long bytes, hipStream_t stream) {
+    WsLease L;
+    if (bytes <= 0) return L;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
         (void)hipGetLastError();
-        return nullptr;
+        return L;
     }
-    if (cap != hipStreamCaptureStatusNone) return nullptr;
+    if (cap != hipStreamCaptureStatusNone) return L;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
-        return nullptr;
+        return L;
     }
-    std::lock_guard<std::mutex> lock(mu);
-    auto& w = spaces[{dev, stream}];
-    if (w.second >= bytes) return static_cast<float*>(w.first);
-    long long want = bytes > 2 * w.second ? bytes : 2 * w.second;
-    if (want > kWorkspaceMax) want = bytes;
-    void* p = nullptr;
-    if (hipMalloc(&p, (size_t)want) != hipSuccess) {
+    WsPool& P = pool_of(dev);
+    std::lock_guard<std::mutex> lock(P.mu);
+    const int n = (int)P.slots.size();
+    std::vector<long long> by(n);
+    std::vector<int> busy(n), state(n), same(n);
+    for (int i = 0; i < n; ++i) {
+        const WsSlot& s = *P.slots[i];
+        by[i] = s.bytes;
+        busy[i] = s.busy;
+        same[i] = s.recorded && s.last == stream;
+        state[i] = 0;
+        if (s.recorded) {
+            const hipError_t q = hipEventQuery(s.done);
+            if (q != hipSuccess) (void)hipGetLastError();      // hipErrorNotReady
+            state[i] = q == hipSuccess ? 1 : 2;
+        }
+    }
+    int wait = 0, grow = 0;
+    const int i = bpt_ws_choose(n, by.data(), busy.data(), state.data(), same.data(), bytes, kPoolSlots, &wait,
+                                &grow);
+    WsSlot* s;
+    if (i == n) {
+        auto fresh = std::make_unique<WsSlot>();
+        if (hipEventCreateWithFlags(&fresh->done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            return L;
+        }
+        P.slots.push_back(std::move(fresh));
+        s = P.slots.back().get();
+    } else {
+        s = P.slots[i].get();
+    }
+    if (grow || s->ptr == nullptr) {
+        void* p = nullptr;
+        const long long want = ws_size_for(bytes, s->bytes);
+        if (hipMalloc(&p, (size_t)want) != hipSuccess) {
+            (void)hipGetLastError();
+            return L;                    // the call runs without a workspace
+        }
+        P.retired_bytes += s->bytes;     // the old buffer (if any) is kept
+        s->ptr = p;
+        s->bytes = want;
+        // a new buffer has no earlier use to wait for; `done` still marks the
+        // old buffer's last use, which the new one does not share
+        wait = 0;
+    }
+    if (wait && hipStreamWaitEvent(stream, s->done, 0) != hipSuccess) {
         (void)hipGetLastError();
-        return nullptr;
+        return L;
     }
-    w = {p, want};
-    return static_cast<float*>(p);
+    s->busy = true;
+    L.pool = &P;
+    L.slot = s;
+    L.ptr = s->ptr;
+    return L;
+}
+
+// Record the buffer's last use on the stream the call's kernels went to.
+void ws_release(WsLease& L, hipStream_t stream) {
+    if (L.slot == nullptr) return;
+    std::lock_guard<std::mutex> lock(L.pool->mu);
+    WsSlot* s = L.slot;
+    if (hipEventRecord(s->done, stream) == hipSuccess) {
+        s->recorded = true;
+        s->last = stream;
+    } else {
+        // its last use cannot be ordered against later calls: keep the
+        // buffer out of the pool for good
+        (void)hipGetLastError();
+        L.pool->retired_bytes += s->bytes;
+        s->ptr = nullptr;
+        s->bytes = 0;
+        s->recorded = false;
+    }
+    s->busy = false;
+    L.slot = nullptr;
 }
 
 // B given transposed: its tiles are K-contiguous like A's, so the same rules
@@ -317,7 +482,7 @@ int choose_pipelined(const Call& c) {
 // the copies, storing C at its true N.  Worth it when the product is large
 // enough for the copies (each operand read and written once) to be small
 // against the guarded kernel's time; limited by the workspace.
-constexpr long long kRepackMax = 1LL << 30;        // workspace bytes per (device, stream)
+constexpr long long kRepackMax = 1LL << 30;        // bytes of padded copies per call
 
 long long round8(long long x) { return (x + 7) / 8 * 8; }
 
@@ -565,11 +730,8 @@ void launch_split_sum(const bpt::SkinnySumArgs& a, int S, hipStream_t stream) {
 template <typename T, typename OutT, bool RING = false>
 hipError_t launch_skinny_wide(const Call& c, hipStream_t stream) {
     int S = RING ? ring_splits(c) : wide_splits(c);
-    float* ws = nullptr;
-    if (S > 1) {
-        ws = stream_workspace(wide_blocks_per_launch(c) * S * 64 * kSwBN * 4, stream);
-        if (ws == nullptr) S = 1;       // S > 1 fits K, so S = 1 does too
-    }
+    float* ws = static_cast<float*>(c.ws);
+    if (ws == nullptr) S = 1;           // S > 1 fits K, so S = 1 does too
     bpt::SkinnyArgs a;
     a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
     a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
@@ -655,15 +817,20 @@ void launch_repack_copy(const void* src, long long ld, long long stride, void* d
         hipLaunchKernelGGL(bpt::repack_pad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
 }
 
-// Copy A and B into the stream's workspace, zero-padded and aligned, then run
-// the pipelined kernel on the copies.  Without a workspace (graph capture,
-// allocation failure) the guarded kernel takes the call as it is.
+// Split-K for few output tiles: the K ranges run as one batched call of a
+// pipelined variant into fp32 partials in the stream's workspace, then the
+// in-order sum kernel writes C.  Without a workspace the call runs unsplit.
 template <typename T, typename OutT>
 hipError_t launch_splitk(const Call& c, hipStream_t stream) {
     const int S = splitk_splits(c);
-    float* ws = S > 1 ? stream_workspace((long long)S * c.M * c.N * 4, stream) : nullptr;
-    if (ws == nullptr) return dispatch_typed<T, OutT>(c, choose_layout(c), stream);   // e.g. graph capture
-    const Call p = splitk_call(c, S, ws);
+    float* ws = S > 1 ? static_cast<float*>(c.ws) : nullptr;
+    if (ws == nullptr) {                // e.g. graph capture
+        Call u = c;
+        u.ws = nullptr;
+        return dispatch_typed<T, OutT>(u, choose_layout(u), stream);
+    }
+    Call p = splitk_call(c, S, ws);
+    p.ws = nullptr;                     // the partial products need none
     hipError_t e = dispatch_typed<T, float>(p, choose_layout(p), stream);
     if (e != hipSuccess) return e;
     bpt::SplitSumArgs a;
@@ -678,12 +845,16 @@ hipError_t launch_splitk(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Copy A and B into the stream's workspace, zero-padded and aligned, then run
+// the pipelined kernel on the copies.  Without a workspace (graph capture,
+// allocation failure) the guarded kernel takes the call as it is.
 template <typename T, typename OutT>
 hipError_t launch_repack(const Call& c, hipStream_t stream) {
     if (repack_bytes(c) == 0) return dispatch_typed<T, OutT>(c, choose_pipelined(c), stream);   // nothing to copy
-    void* ws = stream_workspace(repack_bytes(c), stream);
+    void* ws = c.ws;
     if (ws == nullptr) return launch_generic<T, OutT>(c, stream);
-    const Call r = repacked_call(c, ws);
+    Call r = repacked_call(c, ws);
+    r.ws = nullptr;
     if (repack_a(c))
         launch_repack_copy(c.A, c.lda, c.sA, const_cast<void*>(r.A), r.lda, c.M * r.lda, c.batch, c.M, c.K, c.M,
                            r.K, stream);
@@ -767,6 +938,26 @@ bool variant_accepts(const Call& c, int v) {
     }
 }
 
+// Bytes of workspace the launch of variant v for this call would use (0:
+// none): the fp32 partials of the split-K paths, the padded copies of the
+// repack route.
+long long workspace_need(const Call& c, int v) {
+    if (c.K <= 0) return 0;
+    switch (v) {
+        case V_SKINNY_WIDE:
+        case V_SKINNY_RING: {
+            const int S = v == V_SKINNY_RING ? ring_splits(c) : wide_splits(c);
+            return S > 1 ? wide_blocks_per_launch(c) * S * 64 * kSwBN * 4 : 0;
+        }
+        case V_SPLITK: {
+            const int S = splitk_splits(c);
+            return S > 1 ? (long long)S * c.M * c.N * 4 : 0;
+        }
+        case V_REPACK: return repack_bytes(c);
+        default: return 0;
+    }
+}
+
 bpt_status run(const Call& c, int variant, hipStream_t stream) {
     bpt_status s = validate(c);
     if (s != BPT_OK) return s;
@@ -776,11 +967,15 @@ bpt_status run(const Call& c, int variant, hipStream_t stream) {
     if (c.K > 0 && !variant_accepts(c, v))
         return fail(BPT_ERR_UNSUPPORTED, "variant %s cannot take M=%lld N=%lld K=%lld lda=%lld ldb=%lld",
                     kVariantNames[v], c.M, c.N, c.K, c.lda, c.ldb);
+    Call cw = c;
+    WsLease lease = ws_acquire(workspace_need(c, v), stream);
+    cw.ws = lease.ptr;
     hipError_t e;
     if (c.dtype == 0)
-        e = c.out_fp32 ? dispatch_typed<_Float16, float>(c, v, stream) : dispatch_typed<_Float16, _Float16>(c, v, stream);
+        e = c.out_fp32 ? dispatch_typed<_Float16, float>(cw, v, stream) : dispatch_typed<_Float16, _Float16>(cw, v, stream);
     else
-        e = c.out_fp32 ? dispatch_typed<__bf16, float>(c, v, stream) : dispatch_typed<__bf16, __bf16>(c, v, stream);
+        e = c.out_fp32 ? dispatch_typed<__bf16, float>(cw, v, stream) : dispatch_typed<__bf16, __bf16>(cw, v, stream);
+    ws_release(lease, stream);
     if (e != hipSuccess) return fail(BPT_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return BPT_OK;
 }

@@ -3,7 +3,7 @@
 // for BH independent (batch x head) problems of Sq query rows, Skv keys and
 // head dimension D (128 or 256), fp16 or bf16 in, fp32 accumulation.
 //
-// This is the second workload of the pages: the "Named Barriers" page
+// This is the second workload of the pages: the "Xe2 Nbarrier Pipelining" page
 // (section "Proven Pattern: SDP Kernel Split Barrier B") describes an
 // HD = 256 flash-attention kernel whose loop runs QK products, the softmax,
 // a trip of S through shared memory, then the PV products, with the loads of

@@ -7,12 +7,10 @@ in the caches; inputs uniform in [-1, 1) without zeros, seeded.  One "step"
 is one GEMM call (the whole hot path) on the next buffer set.
 
 Protocol (the "Xe2 ESIMD GEMM" page, "Performance testing" and "Workflow"):
-W untimed warm-up steps, a pause, then exactly K timed steps (default 1000)
+W untimed warm-up steps, a pause, untimed steps until the clock has come
+back from idle (time_steps), then exactly K timed steps (default 1000)
 between two device synchronisations.  The kernel time is measured with HIP
-events recorded on the stream the kernels are launched on.  After the pause
-the clock takes some 20 ms of load to come back up, so short timed blocks
-read low (4096^3: 1090 TFLOP/s over 200 calls, 1190 over 1000, 1216 over
-3000 on the same machine).
+events recorded on the stream the kernels are launched on.
 
 The JSON line also carries
 * roofline: algorithmic flops (or bytes, for the memory-bound shape) per
@@ -48,32 +46,45 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    """Hash of every kernel and launcher source (any change voids the stored
-    counter readings)."""
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "barrier_pipelined_tiled_amd", "csrc")
-    for rel in sorted(os.listdir(csrc)):
-        if rel.endswith((".hpp", ".hip")):
-            with open(os.path.join(csrc, rel), "rb") as f:
-                h.update(rel.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+def kernel_table() -> dict:
+    """The built library's kernels: name -> hash of its machine code and its
+    resource use (written by the build beside the library)."""
+    path = os.path.join(ROOT, "barrier_pipelined_tiled_amd", "libbpt_gemm.kernels.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        return json.load(f)
+
+
+def template_code(table: dict, kernel_name: str):
+    """Hash over the machine code of every instance of the kernel template a
+    profiler's kernel name belongs to (None when the library has none)."""
+    from barrier_pipelined_tiled_amd import asm_info
+    base = asm_info.base_name(kernel_name)
+    if base is None:
+        return None
+    return asm_info.template_hash({n: k["code"] for n, k in table.items()}, base)
 
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per step from the committed counter runs (profiles/traffic.json):
     FETCH_SIZE and WRITE_SIZE per dispatch, summed over the kernels of one
     step and scaled by the copy-kernel calibration; None when no run exists
-    for this variant or the kernel sources changed since it was taken."""
+    for this variant, or when the machine code of any kernel it covers
+    differs from the built library's (each entry records a hash of the code
+    the counters were taken on)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     e = t.get("entries", {}).get(workload)
-    if not e or e.get("variant") != kernel or e.get("source_sha") != kernel_source_sha():
+    if not e or e.get("variant") != kernel:
         return None
+    table = kernel_table()
+    for k in e["kernels"]:
+        if not k.get("code") or template_code(table, k["name"]) != k["code"]:
+            return None
     kib = sum(k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"] for k in e["kernels"])
     return int(round(kib * 1024))
 
@@ -149,7 +160,7 @@ def record_traffic(run_dir: str, path: str | None = None) -> None:
     fetch_scale = copy_kib / cf[ck][0]
     write_scale = copy_kib / cw[ck][0]
     entries = {}
-    sha = kernel_source_sha()
+    table = kernel_table()
     for bj in sorted(glob.glob(os.path.join(run_dir, "bench_*.json"))):
         wname = os.path.basename(bj)[len("bench_"):-len(".json")]
         fe, wr = per_kernel(f"pmc_fetch_{wname}"), per_kernel(f"pmc_write_{wname}")
@@ -157,15 +168,17 @@ def record_traffic(run_dir: str, path: str | None = None) -> None:
             continue
         with open(bj) as fh:
             variant = json.loads(fh.read().strip().splitlines()[-1])["config"]["kernel"]
-        kernels = [{"name": k, "dispatches": fe[k][1], "fetch_kib": round(fe[k][0], 2),
-                    "write_kib": round(wr[k][0], 2)} for k in fe if k in wr]
-        entries[wname] = {"variant": variant, "source_sha": sha, "kernels": kernels}
+        kernels = [{"name": k, "code": template_code(table, k), "dispatches": fe[k][1],
+                    "fetch_kib": round(fe[k][0], 2), "write_kib": round(wr[k][0], 2)} for k in fe if k in wr]
+        entries[wname] = {"variant": variant, "kernels": kernels}
     out = {
         "_comment": "HBM-side traffic per call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                     "(KiB per dispatch, mean over the dispatches of a bench run), one entry per "
                     "kernel of the call, scaled by what the same counters read for a plain copy "
                     f"of 256 MiB (FETCH_SIZE {cf[ck][0]:.2f} KiB, WRITE_SIZE {cw[ck][0]:.2f} KiB). "
-                    "Valid only while the kernel sources hash to source_sha.",
+                    "Written only by bench.py --record-traffic.  An entry is used only while every "
+                    "instance of each of its kernels' templates has the machine code it had when the "
+                    "counters were taken ('code': hash over the instances' gfx950 code).",
         "fetch_scale": fetch_scale,
         "write_scale": write_scale,
         "entries": entries,
@@ -174,7 +187,7 @@ def record_traffic(run_dir: str, path: str | None = None) -> None:
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
-    print(f"wrote {path}: {sorted(entries)} at source {sha}")
+    print(f"wrote {path}: {sorted(entries)}")
 
 
 def parse_smi(text: str) -> dict:
@@ -252,21 +265,53 @@ def clocks_under_load(torch, step, settle_s: float = 2.0, max_s: float = 20.0) -
 
 
 def time_steps(torch, step, args, stream):
-    """The timing protocol: W untimed warm-up steps, the pause, K timed steps
-    between two synchronisations (wall clock and HIP events on the launch
-    stream), then a per-call spread outside the timed block."""
+    """The timing protocol: W untimed warm-up steps, the pause, the settle
+    phase, then K timed steps between two synchronisations (wall clock and
+    HIP events on the launch stream); then a per-call spread outside the
+    timed block.
+
+    The page's pause before timing is there so that the measurement starts
+    at the GPU's steady frequency.  On MI355X a pause does the opposite: the
+    shader clock drops to idle and needs some 50 ms of load to come back (on
+    4096^3: 0.140 ms per call in the first 7 ms after a pause, 0.117 after
+    25 ms, 0.1125 from 50 ms on, flat for the following 4 s).  So the pause
+    is followed by untimed steps for settle_ms of GPU time before the timed
+    block.  The first K steps after the pause are timed too, on their own,
+    and reported as after_pause -- they are not the value."""
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     if args.sleep > 0:
         time.sleep(args.sleep)
+    i = args.warmup
+    settle = None
+    if args.settle_ms > 0:
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.steps):
+            step(i)
+            i += 1
+        a1.record(stream)
+        torch.cuda.synchronize()
+        after_ms = a0.elapsed_time(a1) / args.steps
+        n = max(0, int(args.settle_ms / after_ms) + 1 - args.steps)
+        for _ in range(n):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+        settle = {"after_pause_ms_per_step": after_ms, "settle_ms": args.settle_ms,
+                  "settle_steps": args.steps + n}
+        log(f"after the pause: {after_ms:.4f} ms/step over the first {args.steps} steps; "
+            f"settled with {args.steps + n} untimed steps")
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
+    for _ in range(args.steps):
         step(i)
+        i += 1
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -277,15 +322,16 @@ def time_steps(torch, step, args, stream):
     # its own pair of events on the launch stream
     n_calls = min(50, max(10, args.steps // 4))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
-    for i, (a, b) in enumerate(evs):
+    for a, b in evs:
         a.record(stream)
         step(i)
+        i += 1
         b.record(stream)
     torch.cuda.synchronize()
     per_call = sorted(a.elapsed_time(b) for a, b in evs)
     pct = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
     spread = {"calls": n_calls, "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
-    return ms_per_step, kernel_ms, spread
+    return ms_per_step, kernel_ms, spread, settle
 
 
 def roofline(flops, compulsory_bytes, kernel_ms):
@@ -403,14 +449,17 @@ def attention_setup(torch, pkg, inputs, args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 1000 timed calls: after the pause the clock needs some 20 ms to ramp up
-    # again, which a 200-call block (26 ms at 4096^3) would mostly measure
+    # 1000 timed calls, the page's preferred count for compute-bound kernels
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="f16_4096",
                     help="a GEMM workload (f16_4096, ...) or an attention one (attn_f16_...)")
     ap.add_argument("--variant", type=int, default=0, help="GEMM variant, 0 = automatic choice")
     ap.add_argument("--sleep", type=float, default=5.0, help="pause before timing (s)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps after the pause, in ms of GPU time, so that the timed block "
+                         "starts at the steady clock (0: none; the first --steps steps after the "
+                         "pause are then the timed block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock and power readings")
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
@@ -448,7 +497,7 @@ def main():
     log("inputs resident in HBM")
 
     clk_before = None if args.no_clocks else smi_finish(smi_start())
-    ms_per_step, kernel_ms, spread = time_steps(torch, step, args, stream)
+    ms_per_step, kernel_ms, spread, settle = time_steps(torch, step, args, stream)
     clocks = None
     if not args.no_clocks:
         clocks = {"nominal_gfx_mhz": NOMINAL_GFX_MHZ, "before": clk_before,
@@ -476,6 +525,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_call": spread,
+        "settle": settle,
         "clocks": clocks,
     }
     print(json.dumps(out), flush=True)

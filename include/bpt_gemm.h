@@ -37,15 +37,21 @@
  *     batch strides or bases not 16-byte granular -- with at least 2^24
  *     multiply-adds) copies A and/or B there, zero-padded and aligned
  *     (at most 1 GiB).
- * It is one device buffer per (device, stream), allocated with hipMalloc by
- * the first call on that stream that needs it and replaced by a larger one
- * (at least twice the size) when a later call needs more.  No buffer is
- * freed before the process exits.  Calls on one stream use it in stream
- * order; calls on different streams never share one.  A call made while its
- * stream is being captured into a graph, or one whose allocation fails,
- * takes a path without workspace (the skinny or pipelined kernel unsplit,
- * the guarded kernel instead of the repack) -- so a captured graph never refers to a
- * library buffer.
+ * The buffers come from a pool per device.  Each carries an event recorded
+ * on the caller's stream after the last kernel that used it, and a call
+ * taking a buffer whose event has not completed first makes its stream wait
+ * for it (hipStreamWaitEvent), whatever the stream handles: calls on
+ * different streams -- hipStreamPerThread from several threads, a new
+ * stream that got a destroyed one's handle -- never use a buffer at the same
+ * time.  A buffer is allocated with hipMalloc only when no pooled one is
+ * free and large enough (the first such call on a device, a call needing
+ * more than before, calls in flight on more streams than the pool's 4
+ * buffers); a grown-out buffer is kept until the process exits (hipFree
+ * would synchronise the device).  A call made while its stream is being
+ * captured into a graph, or one whose allocation fails, takes a path
+ * without workspace (the skinny or pipelined kernel unsplit, the guarded
+ * kernel instead of the repack) -- so a captured graph never refers to a
+ * pooled buffer.
  *
  * Execution: the call validates its arguments on the host, enqueues the
  * kernel(s) on `stream` (NULL = the default stream) and returns without
@@ -139,7 +145,7 @@ bpt_status gemm_ex_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                       int out_fp32, int variant, struct ihipStream_t *stream);
 
 /* Fused scaled dot-product attention, forward (the pages' second workload:
- * the HD = 256 flash-attention "SDP" kernel of the "Named Barriers" page,
+ * the HD = 256 flash-attention "SDP" kernel of the "Xe2 Nbarrier Pipelining" page,
  * section "Proven Pattern: SDP Kernel Split Barrier B"):
  *     O[b][i][d] = sum_j p_j V[b][j][d] / sum_j p_j,
  *     p_j = exp(s_j - max_j s_j),  s_j = scale * sum_e Q[b][i][e] K[b][j][e]
@@ -180,6 +186,21 @@ int bpt_select_variant_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_
  * range.  Names spell the tile shape, K-tile and stage count. */
 int bpt_variant_count(void);
 const char *bpt_variant_name(int v);
+
+/* The workspace pool's choice of buffer, exported so that its policy can be
+ * tested without a GPU (the library calls it internally; a caller never
+ * needs to).  Input, for each of the n buffers of a device's pool: bytes[i];
+ * busy[i] (1: taken by a call still on the host); state[i] (0: never used,
+ * 1: its last use has completed, 2: its last use may still run); same[i] (1:
+ * that last use was on the caller's stream handle).  Returns the buffer to
+ * take, or n for a new one.  *wait is set to 1 when the caller's stream must
+ * first wait for the buffer's last use -- always for state 2, since a handle
+ * can name a different stream (hipStreamPerThread on another thread, a
+ * destroyed stream's handle reused) -- and *grow to 1 when the buffer is too
+ * small and is replaced by a larger one.  cap is the pool size above which
+ * calls wait for each other's buffers rather than add one. */
+int bpt_ws_choose(int n, const long long *bytes, const int *busy, const int *state, const int *same,
+                  long long need, int cap, int *wait, int *grow);
 
 /* Static text for a status code. */
 const char *bpt_status_string(bpt_status s);

@@ -260,7 +260,7 @@ void oracle_gemm_at(int dtype, int64_t K,
  *     s_j = scale * sum_{e=0}^{D-1} Q[b][i][e] * K[b][j][e]
  * with j over the Skv keys, no mask.  This is the plain definition of a
  * softmax over the scaled logits followed by the weighted sum of value rows
- * (the "Named Barriers" page, section "Proven Pattern: SDP Kernel Split
+ * (the "Xe2 Nbarrier Pipelining" page, section "Proven Pattern: SDP Kernel Split
  * Barrier B", names this kernel, an HD = 256 flash attention); subtracting
  * the row maximum changes no exact value and keeps exp() finite.
  *

@@ -1,0 +1,229 @@
+"""Static checks of the barrier schedule and resources on the library's own
+gfx950 assembly (kept by the build).  No GPU.
+
+What the pages ask of a split-barrier pipeline, checked on the code the
+compiler actually produced:
+* every wave executes the same barriers ("Xe2 ESIMD GEMM", Hardware limits;
+  "Xe2 Nbarrier Pipelining", What Doesn't Work: Double-Arrive Deadlock): no
+  s_barrier sits in code that only some lanes run (under a saved exec mask),
+  and no loop that holds a barrier changes exec;
+* each publish is one s_barrier right after its wait ("Xe2 Nbarrier
+  Pipelining", Checklist for Adding Split Barriers, steps 6-7): in every
+  kernel that stages tiles by LDS-DMA the barrier follows an
+  s_waitcnt vmcnt(n) lgkmcnt(0), with n one of the wait counts the kernel's
+  ring implies (closed forms of its template parameters below), the steady
+  count inside the K-loop, and the K-loop holds exactly one barrier per
+  K-tile it runs per iteration;
+* no kernel spills ("Xe2 ESIMD GEMM", Workflow step 2): the GEMM kernels use
+  no scratch and spill no VGPR or SGPR.
+"""
+import os
+import re
+
+import pytest
+
+from barrier_pipelined_tiled_amd import asm_info, build
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    if not os.path.exists(build.ASM_PATH):
+        build.build()
+    with open(build.ASM_PATH) as f:
+        return asm_info.kernels(f.read())
+
+
+def _ints(name):
+    """The integer template arguments of a mangled kernel name, in order."""
+    return [int(x) for x in re.findall(r"Li(\d+)E", name)]
+
+
+def expected_waits(name):
+    """(wait counts a publish of this kernel may use, the steady count of its
+    K-loop, barriers per K-loop iteration), from the ring's layout; None for
+    kernels that stage nothing by LDS-DMA."""
+    base = asm_info.base_name(name)
+    if base == "gemm_pipelined_kernel":
+        BM, BN, BK, S = _ints(name)[:4]
+        lps = (BM * BK + BK * BN) // 2048           # 1 KiB copies per wave per stage (4 waves)
+        allowed = {lps * (S - 1)} | {lps * (S - 2 - d) for d in range(S - 1)} | {0}
+        return allowed, lps * (S - 2), 1
+    if base == "gemm_apair_kernel":
+        le, lo = 8 + 4, 4                           # even group: A pair + B; odd group: B
+        return {lo + le + lo, le + lo, lo, 0}, le + lo, 2
+    if base == "gemm_persist_kernel":
+        (nk,) = _ints(name)
+        lps = (256 * 32 + 32 * 128) // 2048
+        return {lps * 2 + lps // 2, lps * 2, 0}, lps * 2, nk
+    if base == "gemm_skinny_ring_kernel":
+        kc, s = _ints(name)[:2]
+        lps = (64 * kc * 2) // 4096 + (kc * 128 * 2) // 4096
+        return {(s - 2) * lps}, (s - 2) * lps, 1
+    if base == "attention_fwd_kernel":
+        d, waves, bn, s = _ints(name)[:4]
+        copies = bn * d * 2 // 1024 // waves
+        return {(s - 2) * 2 * copies}, (s - 2) * 2 * copies, 1
+    return None
+
+
+_EXEC_WRITE = re.compile(r"^(s_\w+_saveexec_b64|v_cmpx_\w+|s_\w+_b64 exec,|s_mov_b64 exec,)")
+
+
+def _loops(lines):
+    """Line-index sets of the kernel's loops (natural loops of its control flow)."""
+    return asm_info.natural_loops(lines)
+
+
+def _barrier_kernels(kernels):
+    return {n: k for n, k in kernels.items() if "s_barrier" in k["lines"]}
+
+
+def test_every_barrier_kernel_is_recognised(kernels):
+    names = _barrier_kernels(kernels)
+    assert names
+    for n in names:
+        if asm_info.base_name(n) not in ("gemm_generic_kernel", "gemm_skinny_kernel"):
+            assert expected_waits(n) is not None, n
+
+
+def check_no_barrier_under_saved_exec(kernels):
+    for n, k in _barrier_kernels(kernels).items():
+        open_masks = []
+        for l in k["lines"]:
+            m = re.match(r"s_and_saveexec_b64 (s\[\d+:\d+\])", l)
+            if m:
+                open_masks.append(m.group(1))
+                continue
+            m = re.match(r"s_or_b64 exec, exec, (s\[\d+:\d+\])", l)
+            if m and m.group(1) in open_masks:
+                open_masks.remove(m.group(1))
+                continue
+            if l == "s_barrier":
+                assert not open_masks, f"{n}: s_barrier under saved exec {open_masks}"
+
+
+def test_no_barrier_under_a_saved_exec_mask(kernels):
+    """Straight-line scan: s_and_saveexec opens a region only some lanes run,
+    the s_or_b64 exec that restores the saved mask closes it.  No barrier may
+    sit inside one."""
+    check_no_barrier_under_saved_exec(kernels)
+
+
+def check_publish_waits(kernels):
+    for n, k in _barrier_kernels(kernels).items():
+        exp = expected_waits(n)
+        if exp is None:
+            continue
+        allowed, steady, per_iter = exp
+        L = k["lines"]
+        bars = [i for i, l in enumerate(L) if l == "s_barrier"]
+        seen = set()
+        for i in bars:
+            m = re.match(r"s_waitcnt vmcnt\((\d+)\) lgkmcnt\(0\)$", L[i - 1])
+            assert m, f"{n}: barrier not preceded by a publish wait: {L[i - 1]!r}"
+            seen.add(int(m.group(1)))
+        assert seen <= allowed, f"{n}: wait counts {sorted(seen)} not in {sorted(allowed)}"
+        assert steady in seen, n
+        # the innermost loop around each barrier is the K-loop: per_iter
+        # barriers, all with the steady count, no exec writes
+        loops = _loops(L)
+        k_loops = []
+        for i in bars:
+            around = [lp for lp in loops if i in lp]
+            if not around:
+                continue                       # prologue, drain or epilogue publish
+            inner = min(around, key=len)
+            if inner not in k_loops:
+                k_loops.append(inner)
+        assert k_loops, f"{n}: no loop holds a barrier"
+        for lp in k_loops:
+            idx = sorted(i for i in lp if L[i] == "s_barrier")
+            assert len(idx) == per_iter, f"{n}: {len(idx)} barriers per K-loop iteration, expected {per_iter}"
+            for j in idx:
+                assert L[j - 1] == f"s_waitcnt vmcnt({steady}) lgkmcnt(0)", (n, L[j - 1])
+            writes = [L[i] for i in sorted(lp) if _EXEC_WRITE.match(L[i])]
+            assert not writes, f"{n}: the K-loop writes exec: {writes[:3]}"
+
+
+def test_publish_waits_match_the_ring(kernels):
+    check_publish_waits(kernels)
+
+
+APAIR = "_ZN3bpt17gemm_apair_kernelIDF16_DF16_Lb0EEEvNS_8GemmArgsE"
+
+
+def _planted(kernels, edit):
+    k = dict(kernels[APAIR])
+    lines = list(k["lines"])
+    loop = min((lp for lp in _loops(lines) if any(lines[i] == "s_barrier" for i in lp)), key=len)
+    a, b = min(loop), max(loop)
+    edit(lines, a, b)
+    k["lines"] = lines
+    return {APAIR: k}
+
+
+def test_the_checks_catch_planted_mistakes(kernels):
+    """Each mistake, planted in a copy of the 4096^3 kernel's K-loop, fails a
+    check: a dropped barrier, a wait that lets one copy too many fly, a wait
+    for LDS reads dropped, an exec write, a barrier in a divergent region."""
+    def first(lines, a, b, what):
+        return next(i for i in range(a, b + 1) if lines[i] == what)
+
+    def drop_barrier(lines, a, b):
+        del lines[first(lines, a, b, "s_barrier")]
+
+    def off_by_one(lines, a, b):
+        i = first(lines, a, b, "s_barrier")
+        lines[i - 1] = "s_waitcnt vmcnt(17) lgkmcnt(0)"
+
+    def no_lds_wait(lines, a, b):
+        i = first(lines, a, b, "s_barrier")
+        lines[i - 1] = "s_waitcnt vmcnt(16)"
+
+    def exec_write(lines, a, b):
+        lines.insert(a + 1, "s_and_saveexec_b64 s[60:61], vcc")
+
+    def divergent(lines, a, b):
+        i = first(lines, a, b, "s_barrier")
+        lines.insert(i - 1, "s_and_saveexec_b64 s[60:61], vcc")
+
+    check_publish_waits({APAIR: kernels[APAIR]})
+    check_no_barrier_under_saved_exec({APAIR: kernels[APAIR]})
+    for edit in (drop_barrier, off_by_one, no_lds_wait, exec_write):
+        with pytest.raises(AssertionError):
+            check_publish_waits(_planted(kernels, edit))
+    with pytest.raises(AssertionError):
+        check_no_barrier_under_saved_exec(_planted(kernels, divergent))
+
+
+GEMM_TEMPLATES = ("gemm_pipelined_kernel", "gemm_apair_kernel", "gemm_persist_kernel", "gemm_skinny_kernel",
+                  "gemm_skinny_ring_kernel", "gemm_generic_kernel", "skinny_sum_kernel", "splitk_sum_kernel",
+                  "repack_pad_kernel", "fill_zero_kernel")
+
+
+def test_gemm_kernels_use_no_scratch_and_spill_nothing(kernels):
+    seen = set()
+    for n, k in kernels.items():
+        base = asm_info.base_name(n)
+        if base not in GEMM_TEMPLATES:
+            continue
+        seen.add(base)
+        m = k["meta"]
+        assert m["private_segment_fixed_size"] == 0, (n, m)
+        assert m["vgpr_spill_count"] == 0, (n, m)
+        if base != "gemm_persist_kernel":       # its SGPRs: the test below
+            assert m["sgpr_spill_count"] == 0, (n, m)
+    assert seen == set(GEMM_TEMPLATES)
+
+
+@pytest.mark.xfail(strict=True, reason="the persistent short-K kernel still spills SGPRs into VGPR lanes "
+                                       "(v_writelane/v_readlane, no memory traffic)")
+def test_persistent_kernel_spills_no_sgpr(kernels):
+    for n, k in kernels.items():
+        if asm_info.base_name(n) == "gemm_persist_kernel":
+            assert k["meta"]["sgpr_spill_count"] == 0, (n, k["meta"])
+
+
+def test_kernels_fit_one_workgroup_in_lds(kernels):
+    for n, k in kernels.items():
+        assert k["meta"]["group_segment_fixed_size"] <= 160 * 1024, n

@@ -1,6 +1,7 @@
 """Host-side bookkeeping of bench.py: the traffic figures it reports are the
 counter readings of a measurement run, scaled by the copy calibration, and
-are withheld once the kernel sources change.  No GPU is used."""
+are withheld once the machine code of the kernels they cover changes.  No
+GPU is used."""
 import json
 import os
 import sys
@@ -27,55 +28,78 @@ def test_record_traffic_scales_and_sums(tmp_path):
     # the copy reads and writes 256 MiB; FETCH_SIZE reads half of it
     _pmc(run / "pmc_copy_fetch", [("copy_kernel(int4 const*)", 131072.0)] * 3)
     _pmc(run / "pmc_copy_write", [("copy_kernel(int4 const*)", 262144.0)] * 3)
-    _pmc(run / "pmc_fetch_w1", [("k1", 100.0), ("k1", 300.0), ("k2", 10.0), ("k2", 10.0)])
-    _pmc(run / "pmc_write_w1", [("k1", 50.0), ("k1", 50.0), ("k2", 4.0), ("k2", 4.0)])
+    k1, k2 = "void bpt::k1<float>()", "_ZN3bpt2k2IfEEvv"       # profilers print either form
+    _pmc(run / "pmc_fetch_w1", [(k1, 100.0), (k1, 300.0), (k2, 10.0), (k2, 10.0)])
+    _pmc(run / "pmc_write_w1", [(k1, 50.0), (k1, 50.0), (k2, 4.0), (k2, 4.0)])
     (run / "bench_w1.json").write_text(json.dumps({"config": {"kernel": "variant_a"}}) + "\n")
     # a workload with a bench line but no counter runs is left out
     (run / "bench_w2.json").write_text(json.dumps({"config": {"kernel": "variant_b"}}) + "\n")
     out = tmp_path / "traffic.json"
-    bench.record_traffic(str(run), str(out))
+    table = {"_ZN3bpt2k1IfEEvv": {"code": "c1"}, "_ZN3bpt2k2IfEEvv": {"code": "c2"}}
+    bench_table = bench.kernel_table
+    bench.kernel_table = lambda: table
+    try:
+        bench.record_traffic(str(run), str(out))
+    finally:
+        bench.kernel_table = bench_table
     t = json.loads(out.read_text())
     assert t["fetch_scale"] == pytest.approx(2.0)
     assert t["write_scale"] == pytest.approx(1.0)
     assert list(t["entries"]) == ["w1"]
     e = t["entries"]["w1"]
-    assert e["variant"] == "variant_a" and e["source_sha"] == bench.kernel_source_sha()
+    assert e["variant"] == "variant_a"
     k = {x["name"]: x for x in e["kernels"]}
-    assert k["k1"]["fetch_kib"] == 200.0 and k["k1"]["write_kib"] == 50.0 and k["k1"]["dispatches"] == 2
-    assert k["k2"]["fetch_kib"] == 10.0 and k["k2"]["write_kib"] == 4.0
+    assert k[k1]["fetch_kib"] == 200.0 and k[k1]["write_kib"] == 50.0 and k[k1]["dispatches"] == 2
+    assert k[k2]["fetch_kib"] == 10.0 and k[k2]["write_kib"] == 4.0
+    # each kernel is stamped with the hash of its template's machine code
+    assert k[k1]["code"] == bench.template_code(table, k1) is not None
+    assert k[k2]["code"] == bench.template_code(table, k2) != k[k1]["code"]
 
 
-def test_measured_traffic_requires_matching_variant_and_sources(tmp_path, monkeypatch):
+def test_measured_traffic_requires_matching_variant_and_code(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0123456789abcdef")
-    entry = {"variant": "v", "source_sha": "0123456789abcdef",
-             "kernels": [{"name": "a", "fetch_kib": 1.0, "write_kib": 2.0},
-                         {"name": "b", "fetch_kib": 3.0, "write_kib": 0.0}]}
-    (prof / "traffic.json").write_text(json.dumps(
-        {"fetch_scale": 2.0, "write_scale": 1.0, "entries": {"w": entry}}))
+    table = {"_ZN3bpt1aIfEEvv": {"code": "x1"}, "_ZN3bpt1aIiEEvv": {"code": "x2"},
+             "_ZN3bpt1bIfEEvv": {"code": "y1"}}
+    monkeypatch.setattr(bench, "kernel_table", lambda: table)
+    entry = {"variant": "v",
+             "kernels": [{"name": "_ZN3bpt1aIfEEvv", "code": bench.template_code(table, "_ZN3bpt1aIfEEvv"),
+                          "fetch_kib": 1.0, "write_kib": 2.0},
+                         {"name": "void bpt::b<float>()", "code": bench.template_code(table, "_ZN3bpt1bIfEEvv"),
+                          "fetch_kib": 3.0, "write_kib": 0.0}]}
+
+    def write():
+        (prof / "traffic.json").write_text(json.dumps(
+            {"fetch_scale": 2.0, "write_scale": 1.0, "entries": {"w": entry}}))
+    write()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     # (1*2 + 2*1) + (3*2 + 0) KiB
     assert bench.measured_traffic("w", "v") == 10 * 1024
     assert bench.measured_traffic("w", "other_variant") is None
     assert bench.measured_traffic("missing", "v") is None
-    entry["source_sha"] = "0" * 16
-    (prof / "traffic.json").write_text(json.dumps(
-        {"fetch_scale": 2.0, "write_scale": 1.0, "entries": {"w": entry}}))
+    # another instance of template a changed its code: the reading is dropped
+    table["_ZN3bpt1aIiEEvv"] = {"code": "x3"}
+    assert bench.measured_traffic("w", "v") is None
+    table["_ZN3bpt1aIiEEvv"] = {"code": "x2"}
+    assert bench.measured_traffic("w", "v") == 10 * 1024
+    # an entry without a code stamp is never used
+    del entry["kernels"][1]["code"]
+    write()
     assert bench.measured_traffic("w", "v") is None
 
 
-def test_kernel_source_sha_follows_the_sources(tmp_path, monkeypatch):
-    csrc = tmp_path / "barrier_pipelined_tiled_amd" / "csrc"
-    csrc.mkdir(parents=True)
-    (csrc / "k.hip").write_text("a")
-    (csrc / "notes.txt").write_text("ignored")
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    h1 = bench.kernel_source_sha()
-    (csrc / "notes.txt").write_text("changed")
-    assert bench.kernel_source_sha() == h1
-    (csrc / "k.hip").write_text("b")
-    assert bench.kernel_source_sha() != h1
+def test_asm_code_hash_ignores_comments_and_label_numbering():
+    from barrier_pipelined_tiled_amd import asm_info
+    a = {"lines": [asm_info._normalise(x) for x in
+                   ["s_mov_b32 s0, 1 ; a comment", ".LBB44_4:", "s_cbranch_scc1 .LBB44_4"]]}
+    b = {"lines": [asm_info._normalise(x) for x in
+                   ["s_mov_b32   s0, 1", ".LBB7_4:", "s_cbranch_scc1 .LBB7_4 ; other"]]}
+    c = {"lines": [asm_info._normalise(x) for x in
+                   ["s_mov_b32 s0, 2", ".LBB7_4:", "s_cbranch_scc1 .LBB7_4"]]}
+    assert asm_info.code_hash(a) == asm_info.code_hash(b) != asm_info.code_hash(c)
+    assert asm_info.base_name("_ZN3bpt17gemm_apair_kernelIDF16_DF16_Lb0EEEvNS_8GemmArgsE") == "gemm_apair_kernel"
+    assert asm_info.base_name("void bpt::gemm_apair_kernel<bool _Accum, false>(bpt::GemmArgs)") == \
+        "gemm_apair_kernel"
 
 
 def test_more_than_one_gpu_is_refused():

@@ -420,10 +420,11 @@ SPLIT_VARIANTS = ["skinny_64x128_w4_k32_s4_splitk", "skinny_64x128_ring_k32_s4_s
 
 @pytest.mark.parametrize("vname", SPLIT_VARIANTS)
 def test_split_k_workspace_streams_and_growth(vname):
-    """The split-K path keeps one workspace per stream: calls on two streams
-    in flight together, and a call that needs a larger workspace after a
-    smaller one, must each give the result of a lone call, bit for bit (the
-    split sums run in a fixed order)."""
+    """The split-K path takes its partials' buffer from a per-device pool
+    whose buffers are ordered by events: calls on two streams in flight
+    together, and a call that needs a larger buffer after a smaller one, must
+    each give the result of a lone call, bit for bit (the split sums run in a
+    fixed order)."""
     v = pkg.variants()[vname]
     shapes = [(64, 256, 2048), (64, 2048, 4096), (32, 1024, 8192)]     # 4-8 splits; growing
     data = []
@@ -448,12 +449,16 @@ def test_split_k_workspace_streams_and_growth(vname):
 
 @pytest.mark.parametrize("vname", SPLIT_VARIANTS)
 def test_split_k_repeated_and_interleaved(vname):
-    """Many split-K calls in a row on one stream -- 2 to 8 splits, with
-    repack calls that overwrite the shared workspace in between -- must each
-    give the lone call's result bit for bit (the partials are added in split
-    order), and that result meets the oracle."""
+    """Many split-K calls in a row on one stream -- 2 to 64 splits, with
+    repack calls that reuse the pooled buffers in between -- must each give
+    the lone call's result bit for bit (the partials are added in split
+    order, in groups of 8 above 8 splits), and that result meets the
+    oracle."""
     v = pkg.variants()[vname]
-    shapes = [(64, 200, 1024), (64, 1024, 2048), (64, 2048, 4096)]      # wide kernel: S = 2, 4, 8
+    # wide kernel: S = 2, 4, 8, 32, 64 (one 64 x 128 block over K = 16384
+    # and 32768: the most splits K allows); the ring kernel takes S = 1 .. 64
+    # by its own rule
+    shapes = [(64, 200, 1024), (64, 1024, 2048), (64, 2048, 4096), (64, 128, 16384), (64, 128, 32768)]
     rp_A = inputs.uniform((257, 129), 7601, nonzero=True).to(DEV)
     rp_B = inputs.uniform((129, 201), 7602, nonzero=True).to(DEV)
     rp_ref = run(rp_A.cpu(), rp_B.cpu(), "f16", True, pkg.variants()["repack_pipelined"])
@@ -479,11 +484,97 @@ def test_split_k_repeated_and_interleaved(vname):
             assert torch.equal(C.cpu(), rp_ref)
 
 
+class _RawStream:
+    """A bare HIP stream handle in the shape the binding takes (.cuda_stream)."""
+    def __init__(self, handle):
+        self.cuda_stream = handle
+
+
+def _hip_runtime():
+    import ctypes
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    hip = ctypes.CDLL(path)          # the runtime this process already uses
+    hip.hipStreamCreate.argtypes = [ctypes.c_void_p]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def test_workspace_streams_created_and_destroyed():
+    """Split-K calls (the skinny workload shape, 4 splits through the
+    automatic choice) each on a new stream destroyed right after the call,
+    while its kernels may still run: a later stream can receive the same
+    handle, and the pool's events must keep its call off the buffer until the
+    earlier kernels are done.  Every result must equal a lone call's bit for
+    bit; the first mismatch fails."""
+    import ctypes
+    hip = _hip_runtime()
+    M, N, K = 64, 8192, 8192
+    A = inputs.uniform((M, K), 7701, nonzero=True)
+    Bs = [inputs.uniform((K, N), 7702 + j, nonzero=True) for j in range(2)]
+    lone = [run(A, B, "f16", False) for B in Bs]
+    Ad, Bds = A.to(DEV), [B.to(DEV) for B in Bs]
+    outs, handles = [], []
+    for rep in range(32):
+        h = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(h)) == 0
+        handles.append(h.value)
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        pkg.gemm_f16(Ad, Bds[rep % 2], C, stream=_RawStream(h.value))
+        assert hip.hipStreamDestroy(h) == 0
+        outs.append((rep % 2, C))
+    torch.cuda.synchronize()
+    say(f"distinct stream handles over 32 streams: {len(set(handles))}")
+    for rep, (j, C) in enumerate(outs):
+        assert torch.equal(C.cpu(), lone[j]), rep
+    m = oracle.compare(lone[0].float().numpy(), oracle.gemm(inputs.bits(A), inputs.bits(Bs[0]), "f16"), K)
+    assert m["ok"], m
+
+
+def test_workspace_per_thread_streams_from_two_threads():
+    """hipStreamPerThread is one handle that names a different stream on
+    each host thread.  Two threads issue split-K calls on it at the same
+    time, with different inputs: every result must equal a lone call's bit
+    for bit."""
+    import threading
+    per_thread = _RawStream(2)                 # hipStreamPerThread
+    M, N, K = 64, 4096, 8192
+    data = []
+    for t in range(2):
+        A = inputs.uniform((M, K), 7711 + t, nonzero=True)
+        B = inputs.uniform((K, N), 7721 + t, nonzero=True)
+        data.append((A, B, run(A, B, "f16", True)))
+    dev_data = [(A.to(DEV), B.to(DEV)) for A, B, _ in data]
+    outs = [[], []]
+    errors = []
+
+    def worker(t):
+        try:
+            Ad, Bd = dev_data[t]
+            for rep in range(40):
+                C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+                pkg.gemm_ex(Ad, Bd, C, out_fp32=True, stream=per_thread)
+                outs[t].append(C)
+        except Exception as exc:               # reported below, in the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(2):
+        assert len(outs[t]) == 40
+        for rep, C in enumerate(outs[t]):
+            assert torch.equal(C.cpu(), data[t][2]), (t, rep)
+
+
 # split-K over the pipelined kernel's batch: M > 128, at most 128 tiles of
 # 128 x 128, K a multiple of 64 * S with K / S >= 256.  Ragged M and N;
-# S = 4, 8, 2, 8, 2, 4 and 32 below
+# S = 4, 8, 2, 8, 2, 4, 32 and 64 below
 SHAPES_SPLITK = [(256, 1024, 1024), (300, 520, 2048), (129, 136, 512), (640, 768, 4096), (200, 8192, 1024),
-                 (1024, 1024, 8192), (256, 512, 32768)]
+                 (1024, 1024, 8192), (256, 512, 32768), (256, 256, 16384)]     # ... and 64
 
 
 @pytest.mark.parametrize("dtype,out_fp32", [("f16", False), ("f16", True), ("bf16", True), ("bf16", False)])
