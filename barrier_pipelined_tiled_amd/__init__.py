@@ -13,7 +13,8 @@ import ctypes
 import os
 
 __all__ = [
-    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt", "attention_fwd",
+    "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt", "gemm_ex_noalloc",
+    "attention_fwd",
     "variants", "select_variant", "LIB_PATH",
 ]
 
@@ -48,9 +49,13 @@ def lib() -> ctypes.CDLL:
     L.gemm_batched_f16.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, p]
     L.gemm_ex.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
     L.gemm_ex_bt.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
+    L.gemm_ex_noalloc.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, ci, ci, p]
+    L.bpt_noalloc_scratch_bytes.argtypes = []
+    L.bpt_noalloc_scratch_bytes.restype = i64
     L.attention_fwd.argtypes = [ci, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
                                 p, i64, i64, ctypes.c_float, ci, p]
-    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex, L.gemm_ex_bt, L.attention_fwd):
+    for fn in (L.gemm_f16, L.gemm_bf16, L.gemm_batched_f16, L.gemm_ex, L.gemm_ex_bt, L.gemm_ex_noalloc,
+               L.attention_fwd):
         fn.restype = ci
     L.bpt_select_variant.argtypes = [ci, i64, i64, i64, i64, p, i64, p, i64, ci]
     L.bpt_select_variant.restype = ci
@@ -110,7 +115,7 @@ _DT = {"f16": 0, "bf16": 1}
 
 
 def gemm_ex(A, B, C=None, *, dtype: str = "f16", out_fp32: bool = False, variant: int = 0,
-            stream=None):
+            stream=None, _entry: str = "ex"):
     """C = A @ B through gemm_ex.  A (M,K) or (b,M,K), B (K,N) or (b,K,N);
     C is allocated when None.  Returns C."""
     torch = _torch()
@@ -133,9 +138,17 @@ def gemm_ex(A, B, C=None, *, dtype: str = "f16", out_fp32: bool = False, variant
     if (Mc, Nc, bC) != (M, N, bA):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(bA, M, N)}")
     L = lib()
-    _check(L.gemm_ex(_DT[dtype], bA, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
-                     C.data_ptr(), ldc, sC, int(out_fp32), int(variant), _stream_handle(stream)))
+    fn = L.gemm_ex_noalloc if _entry == "noalloc" else L.gemm_ex
+    _check(fn(_DT[dtype], bA, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
+              C.data_ptr(), ldc, sC, int(out_fp32), int(variant), _stream_handle(stream)))
     return C
+
+
+def gemm_ex_noalloc(A, B, C, *, dtype: str = "f16", out_fp32: bool = False, variant: int = 0,
+                    stream=None):
+    """C = A @ B through gemm_ex_noalloc (no device allocation in the call;
+    scratch in the library's fixed device array).  C must be given."""
+    return gemm_ex(A, B, C, dtype=dtype, out_fp32=out_fp32, variant=variant, stream=stream, _entry="noalloc")
 
 
 def gemm_ex_bt(A, Bt, C=None, *, dtype: str = "f16", out_fp32: bool = False, variant: int = 0,

@@ -980,6 +980,66 @@ bpt_status run(const Call& c, int variant, hipStream_t stream) {
     return BPT_OK;
 }
 
+// ---- the no-allocation entry point (gemm_ex_noalloc) -------------------------
+// For callers that cannot allocate (code under graph capture, loops that must
+// not call hipMalloc): the split-K partials and repack copies go into one
+// file-scope device array instead of the pool.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address on the current
+// GPU comes from hipGetSymbolAddress, taken once per device on the first call
+// there and kept; only that address is ever handed to a kernel.
+constexpr long long kScratchBytes = 32LL << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+void* scratch_on_device(int dev) {
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = ptrs.find(dev);
+    if (it != ptrs.end()) return it->second;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    ptrs[dev] = ptr;
+    return ptr;
+}
+
+bpt_status run_noalloc(const Call& c, int variant, hipStream_t stream) {
+    bpt_status s = validate(c);
+    if (s != BPT_OK) return s;
+    if (variant < 0 || variant > V_COUNT) return fail(BPT_ERR_INVALID_ARG, "no variant %d", variant);
+    if (c.batch == 0 || c.M == 0 || c.N == 0) return BPT_OK;
+    int v = variant == V_AUTO ? choose(c) : variant;
+    if (c.K > 0 && !variant_accepts(c, v))
+        return fail(BPT_ERR_UNSUPPORTED, "variant %s cannot take M=%lld N=%lld K=%lld lda=%lld ldb=%lld",
+                    kVariantNames[v], c.M, c.N, c.K, c.lda, c.ldb);
+    const long long need = workspace_need(c, v);
+    if (need > kScratchBytes)
+        return fail(BPT_ERR_UNSUPPORTED,
+                    "variant %s needs %lld bytes of scratch for M=%lld N=%lld K=%lld batch=%lld; the "
+                    "no-allocation entry point has %lld (use gemm_ex, or split the call)",
+                    kVariantNames[v], need, c.M, c.N, c.K, c.batch, kScratchBytes);
+    Call cw = c;
+    if (need > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(BPT_ERR_HIP, "hipGetDevice failed");
+        }
+        cw.ws = scratch_on_device(dev);
+        if (cw.ws == nullptr) return fail(BPT_ERR_HIP, "hipGetSymbolAddress of the scratch array failed");
+    }
+    hipError_t e;
+    if (c.dtype == 0)
+        e = c.out_fp32 ? dispatch_typed<_Float16, float>(cw, v, stream) : dispatch_typed<_Float16, _Float16>(cw, v, stream);
+    else
+        e = c.out_fp32 ? dispatch_typed<__bf16, float>(cw, v, stream) : dispatch_typed<__bf16, __bf16>(cw, v, stream);
+    if (e != hipSuccess) return fail(BPT_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+    return BPT_OK;
+}
+
 // ---------------------------------------------------------------------------
 // attention: O = softmax(scale Q K^T) V
 // ---------------------------------------------------------------------------
@@ -1084,6 +1144,17 @@ bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
     Call c{dtype, batch, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, A, B, C, out_fp32};
     return run(c, variant, reinterpret_cast<hipStream_t>(stream));
 }
+
+bpt_status gemm_ex_noalloc(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, int64_t strideA,
+                           const void* B, int64_t ldb, int64_t strideB,
+                           void* C, int64_t ldc, int64_t strideC,
+                           int out_fp32, int variant, struct ihipStream_t* stream) {
+    Call c{dtype, batch, M, N, K, lda, ldb, ldc, strideA, strideB, strideC, A, B, C, out_fp32};
+    return run_noalloc(c, variant, reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t bpt_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 bpt_status gemm_ex_bt(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                       const void* A, int64_t lda, int64_t strideA,

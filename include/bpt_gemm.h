@@ -125,6 +125,31 @@ bpt_status gemm_ex(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
                    void *C, int64_t ldc, int64_t strideC,
                    int out_fp32, int variant, struct ihipStream_t *stream);
 
+/* For callers that cannot allocate device memory -- code being captured
+ * into a HIP graph, serving loops that must not call hipMalloc, harnesses
+ * that forbid it: gemm_ex with the same arguments, meaning and variant
+ * choice, whose split-K partials and repack copies go into one fixed device
+ * array of bpt_noalloc_scratch_bytes() (32 MiB) instead of the workspace
+ * pool.  It calls no hipMalloc, hipFree or other allocating routine; each
+ * GPU the library runs on holds its copy of the array until the process
+ * ends.  A call whose path needs more scratch than that returns
+ * BPT_ERR_UNSUPPORTED before launching anything (the message names the need
+ * and the limit); calls needing none behave exactly as gemm_ex.  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different host threads without ordering
+ * between them) race and give wrong results.  Calls on one stream are
+ * ordered by the stream.  Nothing in the array has to start at zero (every
+ * partial and copy is written whole before it is read).  Under graph
+ * capture the split paths keep their splits (gemm_ex runs them unsplit). */
+bpt_status gemm_ex_noalloc(int dtype, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda, int64_t strideA,
+                           const void *B, int64_t ldb, int64_t strideB,
+                           void *C, int64_t ldc, int64_t strideC,
+                           int out_fp32, int variant, struct ihipStream_t *stream);
+
+/* Bytes of the no-allocation entry point's device array. */
+int64_t bpt_noalloc_scratch_bytes(void);
+
 /* B given transposed: C (M x N) <- A * Bt^T, where Bt is N x K row major
  * with leading dimension ldbt >= max(1, K) and batch stride strideBt (B is
  * read as B[k][n] = Bt[n][k]).  This is the layout in which the pages' GEMM

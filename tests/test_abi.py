@@ -292,3 +292,16 @@ def test_attention_empty_calls_are_noops(L):
     # nothing to compute: OK, no launch, NULL pointers allowed
     assert _attn(L, BH=0, Q=0, K=0, V=0, O=0) == pkg.BPT_OK
     assert _attn(L, Sq=0, Q=0, K=0, V=0, O=0) == pkg.BPT_OK
+
+
+def test_noalloc_rejects_a_call_needing_more_scratch(L):
+    """The no-allocation entry point refuses, before any launch, a call whose
+    path needs more scratch than its fixed array: 4096 x 4095 x 4090 takes
+    the repack route, whose padded copies of A and B need 64 MiB."""
+    assert L.bpt_noalloc_scratch_bytes() == 32 << 20
+    M, N, K = 4096, 4095, 4090
+    FAKEP = 1 << 20
+    st = L.gemm_ex_noalloc(0, 1, M, N, K, FAKEP, K, 0, FAKEP, N, 0, FAKEP, N, 0, 0, 0, None)
+    assert st == pkg.BPT_ERR_UNSUPPORTED
+    msg = L.bpt_last_error().decode()
+    assert "scratch" in msg and str(32 << 20) in msg
