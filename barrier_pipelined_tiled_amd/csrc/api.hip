@@ -1077,13 +1077,20 @@ hipError_t launch_attention(const AttnCall& c, hipStream_t stream) {
         hipLaunchKernelGGL(kernel, dim3((unsigned)(a.q_tiles * c.BH)), dim3(64 * waves), 0, stream, a);
     };
     constexpr int W256 = kAttnWaves256, B256 = kAttnBlock256, S256 = kAttnStages256;
+    constexpr int W128 = kAttnWaves128, B128 = kAttnBlock128, S128 = kAttnStages128;
+    // the instance with a masked last block only when Skv leaves one
     if (c.D == 256) {
-        if (pos) go(bpt::attention_fwd_kernel<T, 256, OutT, true, W256, B256, S256>, W256);
-        else go(bpt::attention_fwd_kernel<T, 256, OutT, false, W256, B256, S256>, W256);
+        const bool ragged = c.Skv % B256 != 0;
+        if (pos && ragged) go(bpt::attention_fwd_kernel<T, 256, OutT, true, W256, B256, S256, true>, W256);
+        else if (pos) go(bpt::attention_fwd_kernel<T, 256, OutT, true, W256, B256, S256, false>, W256);
+        else if (ragged) go(bpt::attention_fwd_kernel<T, 256, OutT, false, W256, B256, S256, true>, W256);
+        else go(bpt::attention_fwd_kernel<T, 256, OutT, false, W256, B256, S256, false>, W256);
     } else {
-        constexpr int W = kAttnWaves128, B = kAttnBlock128, S = kAttnStages128;
-        if (pos) go(bpt::attention_fwd_kernel<T, 128, OutT, true, W, B, S>, W);
-        else go(bpt::attention_fwd_kernel<T, 128, OutT, false, W, B, S>, W);
+        const bool ragged = c.Skv % B128 != 0;
+        if (pos && ragged) go(bpt::attention_fwd_kernel<T, 128, OutT, true, W128, B128, S128, true>, W128);
+        else if (pos) go(bpt::attention_fwd_kernel<T, 128, OutT, true, W128, B128, S128, false>, W128);
+        else if (ragged) go(bpt::attention_fwd_kernel<T, 128, OutT, false, W128, B128, S128, true>, W128);
+        else go(bpt::attention_fwd_kernel<T, 128, OutT, false, W128, B128, S128, false>, W128);
     }
     return hipGetLastError();
 }

@@ -90,8 +90,13 @@ struct AttnFwd {
 __device__ inline int attn_swz_k(int row) { return row & 15; }
 
 // POS: scale >= 0 (the row maximum of the logits is the maximum of the raw
-// products; for a negative scale it is the minimum).
-template <typename T, int D, typename OutT, bool POS, int WAVES, int BN_, int STAGES>
+// products; for a negative scale it is the minimum).  RAGGED: Skv is not a
+// multiple of BN, and the last block runs as a masked copy of the block code
+// after the loop.  The host picks the instance, so the loop has no
+// condition on it ("Xe2 ESIMD GEMM", Inner-loop rules): at D = 256 the
+// masked copy makes the compiler spill O registers around the loop exit,
+// and only the RAGGED instance pays for that.
+template <typename T, int D, typename OutT, bool POS, int WAVES, int BN_, int STAGES, bool RAGGED>
 __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a) {
     typedef AttnFwd<T, D, WAVES, BN_, STAGES> G;
     typedef typename Mfma<T>::frag_t frag_t;
@@ -287,15 +292,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         };
 #pragma unroll
         for (int b = 0; b < STAGES - 1; ++b) issue(b);
-        const bool ragged = (Skv % BN) != 0;
-        const int nfull = ragged ? nblk - 1 : nblk;
+        // host: RAGGED == (Skv % BN != 0)
+        const int nfull = RAGGED ? nblk - 1 : nblk;
         int j = 0;
         for (; j < nfull; ++j) {
             publish();
             issue(j + STAGES - 1);
             block.template operator()<false>(j);
         }
-        if (ragged) {
+        if constexpr (RAGGED) {
             publish();
             block.template operator()<true>(j);
         }

@@ -227,3 +227,17 @@ def test_persistent_kernel_spills_no_sgpr(kernels):
 def test_kernels_fit_one_workgroup_in_lds(kernels):
     for n, k in kernels.items():
         assert k["meta"]["group_segment_fixed_size"] <= 160 * 1024, n
+
+
+def test_attention_without_a_ragged_tail_spills_nothing(kernels):
+    """The attention instances for Skv a multiple of the key block (the
+    workload's 4096 keys) have no masked copy of the block code after the
+    loop, use no scratch and spill nothing; the RAGGED instances may spill
+    around their masked last block."""
+    seen = 0
+    for n, k in kernels.items():
+        if asm_info.base_name(n) == "attention_fwd_kernel" and n.endswith("Lb0EEEvNS_8AttnArgsE"):
+            seen += 1
+            m = k["meta"]
+            assert m["private_segment_fixed_size"] == 0 and m["vgpr_spill_count"] == 0, (n, m)
+    assert seen == 16                          # {f16, bf16} x {16-bit, fp32 out} x {+,- scale} x {D 128, 256}

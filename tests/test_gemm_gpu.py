@@ -743,6 +743,87 @@ def test_full_size_exact_integers(name):
         assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
 
 
+@pytest.mark.parametrize("name,kind", [("f16_skinny_64x8192x8192", "random"), ("f16_skinny_64x8192x8192", "exact"),
+                                       ("f16_4096", "random"), ("f16_4096", "exact")])
+def test_full_size_whole_output(name, kind):
+    """Every output of a full-size workload against the oracle's whole
+    product, where the oracle finishes in seconds to half a minute on the
+    host: the skinny workload (last rotating set) and one 4096^3 set.
+    Random inputs: the tolerance; integer inputs in [-2, 2]: bitwise (fp16
+    RNE encoding of the exact sums)."""
+    w = inputs.WORKLOADS[name]
+    j = w.rotating - 1
+    say(f"[whole] {name} set {j} {kind}")
+    if kind == "random":
+        A, B = w.make_a(j), w.make_b(j)
+    else:
+        A = inputs.small_integers(w.a_shape(), 8101, dtype=w.dtype)
+        B = inputs.small_integers(w.b_shape(), 8102, dtype=w.dtype)
+    got = pkg.gemm_f16(A.to(DEV), B.to(DEV), out_fp32=w.out_fp32)
+    torch.cuda.synchronize()
+    got = got.cpu()
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B), w.dtype)
+    if kind == "random":
+        m = oracle.compare(got.float().numpy(), ref, w.K)
+        say(f"[whole] {name} rel_rms={m['rel_rms']:.3e} max_abs={m['max_abs']:.3e} nonfinite={m['nonfinite']}")
+        assert m["ok"], m
+    else:
+        assert np.array_equal(as_bits(got), oracle.encode(ref, w.dtype))
+
+
+# The pipelined variants differ only in ring depth, K-tile width, tile size,
+# whether A is staged in pairs and the layout B arrives in.  Each output is
+# still the same sequence of 32x32x16 MFMAs over ascending 16-wide k-steps,
+# so on the same random inputs they must agree bit for bit: a race (a stage
+# read before it was published, or overwritten while still read) would show
+# as a difference between schedules.
+SCHED_FAMILY = ["pipelined_256x256x64_s2", "pipelined_128x128x64_s2", "pipelined_256x256x32_s4",
+                "pipelined_256x256x32_s5", "pipelined_128x128x32_s4", "pipelined_256x256x32_s4_apair"]
+SCHED_FAMILY_BT = ["pipelined_bt_256x256x32_s4", "pipelined_bt_128x128x32_s4", "pipelined_bt_256x256x64_s2",
+                   "pipelined_bt_256x256x32_s4_apair"]
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (640, 768, 1024), (4096, 4096, 4096)])
+@pytest.mark.parametrize("out_fp32", [False, True])
+def test_schedules_give_bitwise_identical_results(M, N, K, out_fp32):
+    say(f"[schedules] M={M} N={N} K={K} out_fp32={out_fp32}")
+    A = inputs.uniform((M, K), 8401 + K, nonzero=True).to(DEV)
+    B = inputs.uniform((K, N), 8402 + K, nonzero=True).to(DEV)
+    Bt = B.t().contiguous()
+    V = pkg.variants()
+    outs = {}
+    for vname in SCHED_FAMILY:
+        outs[vname] = pkg.gemm_ex(A, B, out_fp32=out_fp32, variant=V[vname])
+    for vname in SCHED_FAMILY_BT:
+        outs[vname] = pkg.gemm_ex_bt(A, Bt, out_fp32=out_fp32, variant=V[vname])
+    torch.cuda.synchronize()
+    view = torch.int32 if out_fp32 else torch.int16
+    ref_name = "pipelined_256x256x32_s4"
+    ref = outs[ref_name].cpu().view(view)
+    for vname, C in outs.items():
+        diff = (C.cpu().view(view) != ref).sum().item()
+        assert diff == 0, f"{vname} differs from {ref_name} in {diff} outputs"
+    m = oracle.compare(outs[ref_name].float().cpu().numpy()[:64], oracle.gemm(
+        inputs.bits(A[:64].cpu()), inputs.bits(B.cpu()), "f16"), K)
+    assert m["ok"], m
+
+
+def test_persistent_schedule_matches_the_pipelined_kernel_bitwise():
+    """The persistent short-K kernel (a ring running across tiles, C of a
+    tile stored during the next) against the pipelined kernel on the same
+    batched inputs: bitwise identical."""
+    V = pkg.variants()
+    batch, M, N, K = 32, 512, 512, 256
+    A = inputs.uniform((batch, M, K), 8501, nonzero=True).to(DEV)
+    B = inputs.uniform((batch, K, N), 8502, nonzero=True).to(DEV)
+    p = pkg.gemm_ex(A, B, variant=V["persistent_256x128x32_shortk"])
+    q = pkg.gemm_ex(A, B, variant=V["pipelined_256x256x32_s4"])
+    r = pkg.gemm_ex(A, B, variant=V["pipelined_128x128x32_s4"])
+    torch.cuda.synchronize()
+    assert torch.equal(p.cpu().view(torch.int16), q.cpu().view(torch.int16))
+    assert torch.equal(p.cpu().view(torch.int16), r.cpu().view(torch.int16))
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (96, 8192, 2048), (65, 1000, 1024), (64, 512, 65536),
                                    (64, 256, 8192)])
 def test_mid_rows_take_the_ring_kernel_exactly(M, N, K):
