@@ -32,6 +32,10 @@
 // last one go through a descriptor with no records (zeros, no memory
 // traffic), so the loop has one form and every wait count stays constant.
 //
+// Walk: the workgroups of one XCD take turns along one contiguous eighth of
+// the tiles (persist_logical), so with a batch that is a multiple of 8 each
+// XCD owns whole batch entries and its L2 fetches their A and B once.
+//
 // Host: M % 256 == 0, N % 128 == 0, K == 32 * NK, 16-byte aligned rows,
 // gridDim.x <= total tiles.
 #pragma once
@@ -41,6 +45,40 @@
 #include "gemm_pipelined.hpp"
 
 namespace bpt {
+
+// The logical tile (batch entry major, then the grouped walk inside it) that
+// workgroup wg of `grid` computes on its it-th turn, or -1 when it has none.
+// Workgroups go to the XCDs round-robin (wg % 8).  When grid is a multiple
+// of 8, XCD x owns logical tiles [x*E, (x+1)*E) with E = ceil(total / 8),
+// taken by its grid/8 workgroups in turn, so the tiles it holds at any time
+// are consecutive in the walk and, with 8 | batch, all of its tiles belong
+// to batch entries no other XCD reads.  Otherwise: tile wg + it*grid.
+__device__ inline int persist_logical(int wg, int grid, int it, int total) {
+    if ((grid & 7) == 0) {
+        const int per_xcd = (total + 7) >> 3;
+        const int hi = min(total, ((wg & 7) + 1) * per_xcd);
+        const int L = (wg & 7) * per_xcd + (wg >> 3) + it * (grid >> 3);
+        return L < hi ? L : -1;
+    }
+    const int L = wg + it * grid;
+    return L < total ? L : -1;
+}
+
+// How many turns workgroup wg has: the its with persist_logical >= 0.
+__device__ inline int persist_turns(int wg, int grid, int total) {
+    int first, end, step;
+    if ((grid & 7) == 0) {
+        const int per_xcd = (total + 7) >> 3;
+        first = (wg & 7) * per_xcd + (wg >> 3);
+        end = min(total, ((wg & 7) + 1) * per_xcd);
+        step = grid >> 3;
+    } else {
+        first = wg;
+        end = total;
+        step = grid;
+    }
+    return first < end ? (end - first + step - 1) / step : 0;
+}
 
 template <typename T, typename OutT, int NK>
 __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int total) {
@@ -71,7 +109,9 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int
     const int wn = wave % 2;
     const int lda = args.lda, ldb = args.ldb, ldc = args.ldc, K = args.K;
     const int per = args.tiles_m * args.tiles_n;
-    if ((int)blockIdx.x >= total) return;  // host: gridDim.x <= total; uniform
+    const int wg = blockIdx.x, grid = gridDim.x;
+    const int turns = persist_turns(wg, grid, total);
+    if (turns == 0) return;                // host: grid <= total; uniform
 
     // copy offsets relative to the tile's corner (the descriptors start there)
     uint32_t voffA[G::A_INST_W];
@@ -108,41 +148,60 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int
     }
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
-    // tile number `it` of this workgroup: its batch entry and corner, and
-    // descriptors starting at the corner (no records past the last tile)
+    // the batch entry and corner of logical tile L.  The divisions run on a
+    // VGPR copy of L (every lane the same) and only the results come back
+    // to SGPRs: their temporaries would otherwise take the SGPRs that hold
+    // the two tiles' descriptors across the loop, and spill.
+    auto corner = [&](int L, int& batch, int& m0, int& n0) __attribute__((always_inline)) {
+        int Lv;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(Lv) : "s"(L));
+        const int bv = Lv / per;
+        int tm, tn;
+        group_walk(Lv - bv * per, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+        batch = __builtin_amdgcn_readfirstlane(bv);
+        m0 = __builtin_amdgcn_readfirstlane(tm) * BM;
+        n0 = __builtin_amdgcn_readfirstlane(tn) * BN;
+    };
+    // tile number `it` of this workgroup: descriptors starting at its corner
+    // (no records past the last tile) and this wave's corner of its C
     struct Tile {
-        int batch, m0, n0;
         int4_t ra, rb;
+        OutT* c;
     };
     auto tile_at = [&](int it) __attribute__((always_inline)) {
         Tile t;
-        const int L = blockIdx.x + it * gridDim.x;
-        if (L < total) {
-            t.batch = L / per;
-            int tm, tn;
-            tile_of(L - t.batch * per, per, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
-            t.m0 = tm * BM;
-            t.n0 = tn * BN;
-            const T* a0 = static_cast<const T*>(args.A) + t.batch * args.strideA + (long long)t.m0 * lda;
-            const T* b0 = static_cast<const T*>(args.B) + t.batch * args.strideB + t.n0;
+        const int L = persist_logical(wg, grid, it, total);
+        if (L >= 0) {
+            int batch, m0, n0;
+            corner(L, batch, m0, n0);
+            const T* a0 = static_cast<const T*>(args.A) + batch * args.strideA + (long long)m0 * lda;
+            const T* b0 = static_cast<const T*>(args.B) + batch * args.strideB + n0;
             t.ra = make_rsrc(a0, (uint32_t)(((BM - 1) * (long long)lda + K) * 2));
             t.rb = make_rsrc(b0, (uint32_t)(((K - 1) * (long long)ldb + BN) * 2));
+            t.c = static_cast<OutT*>(args.C) + batch * args.strideC + (long long)(m0 + wm * G::TM) * ldc + n0 +
+                  wn * G::TN;
         } else {
-            t.batch = t.m0 = t.n0 = 0;
             t.ra = t.rb = make_rsrc(args.A, 0u);
+            t.c = nullptr;
         }
         return t;
     };
 
     // copy i (A copies first) of the group of K-tile kt of tile t, into
     // stage kt % STAGES
+    // (the LDS base and the B row step pass through an empty asm so that the
+    // compiler recomputes each copy's destination and k offset with one
+    // scalar op instead of holding all 4 stages x 6 copies x 8 K-tiles of
+    // them in SGPRs across the tile loop, which spilled)
     auto dma_one = [&](const Tile& t, int i, int kt) __attribute__((always_inline)) {
-        const uint32_t sbase = lds0 + (kt % STAGES) * G::STAGE_BYTES;
+        uint32_t l0 = lds0, bstep = b_step;
+        asm volatile("" : "+s"(l0), "+s"(bstep));
+        const uint32_t sbase = l0 + (kt % STAGES) * G::STAGE_BYTES;
         if (i < G::A_INST_W)
             dma16(t.ra, sbase + (wave * G::A_INST_W + i) * 1024, voffA[i], kt * a_step);
         else
             dma16(t.rb, sbase + G::A_STAGE * 2 + (wave * G::B_INST_W + (i - G::A_INST_W)) * 1024,
-                  voffB[i - G::A_INST_W], kt * b_step);
+                  voffB[i - G::A_INST_W], kt * bstep);
     };
 
     float16_t acc[MB][NB];
@@ -221,12 +280,11 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int
             sv[h] = (r & 16) ? int4_t{v[2], v[3], v[0], v[1]} : v;     // undo the half swap
         }
     };
-    auto store_slice = [&](int sl, const Tile& pt) __attribute__((always_inline)) {
-        OutT* Cb = static_cast<OutT*>(args.C) + pt.batch * args.strideC;
+    auto store_slice = [&](int sl, OutT* pc) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < SPS; ++h) {
             const int r = (sl * SPS + h) * 8 + lane / 8;
-            OutT* dst = Cb + (long long)(pt.m0 + wm * G::TM + r) * ldc + pt.n0 + wn * G::TN + (lane % 8) * 8;
+            OutT* dst = pc + (long long)r * ldc + (lane % 8) * 8;
             __builtin_nontemporal_store(sv[h], (int4_t*)dst);
         }
     };
@@ -235,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int
     // (every K-tile's first k-step issues the other slice of group kt+3)
     Tile cur = tile_at(0);
     Tile nxt = tile_at(1);
-    Tile prv = cur;                        // the tile in the staging area (none yet)
+    OutT* prv = cur.c;                     // this wave's C of the tile in the staging area
 #pragma unroll
     for (int g = 0; g < STAGES - 1; ++g)
 #pragma unroll
@@ -263,17 +321,19 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(GemmArgs args, int
         kstep.template operator()<false>(1, (KT + 1) % STAGES, 0, wt, 0, WK % NK);
     };
 
-    for (int it = 0; blockIdx.x + it * gridDim.x < total; ++it) {
+    for (int it = 0; it < turns; ++it) {
         [&]<int... KT>(std::integer_sequence<int, KT...>) {
             (ktile.template operator()<KT>(it), ...);
         }(std::make_integer_sequence<int, NK>{});
-        prv = cur;
+        prv = cur.c;
         cur = nxt;
         nxt = tile_at(it + 2);
     }
     // the copies past the last tile read zeros; the epilogue's publish<0>
     // lets them land before it reuses LDS, then stores the last tile
-    pipelined_epilogue<G, OutT>(args, acc, lds, lane, wave, wm, wn, prv.m0, prv.n0, prv.batch);
+    int lb, lm0, ln0;
+    corner(persist_logical(wg, grid, turns - 1, total), lb, lm0, ln0);
+    pipelined_epilogue<G, OutT>(args, acc, lds, lane, wave, wm, wn, lm0, ln0, lb);
 }
 
 }  // namespace bpt

@@ -62,16 +62,11 @@ struct GemmArgs {
 //
 // Workgroups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
 // its own L2.  The id is first permuted so that XCD x receives a contiguous
-// run of logical ids, then logical ids walk the tile grid in groups of
-// group_m tile-rows, column by column inside a group, so the tiles one XCD
-// holds at a time share few A row-panels and B column-panels.
+// run of logical ids (tile_of), then logical ids walk the tile grid in groups
+// of group_m tile-rows, column by column inside a group (group_walk), so the
+// tiles one XCD holds at a time share few A row-panels and B column-panels.
 // ---------------------------------------------------------------------------
-__device__ inline void tile_of(int pid, int num, int tiles_m, int tiles_n, int group_m,
-                               int& tm, int& tn) {
-    if ((num & 7) == 0) {
-        int per_xcd = num >> 3;
-        pid = (pid & 7) * per_xcd + (pid >> 3);
-    }
+__device__ inline void group_walk(int pid, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
     int per_group = group_m * tiles_n;
     int group = pid / per_group;
     int first_m = group * group_m;
@@ -79,6 +74,15 @@ __device__ inline void tile_of(int pid, int num, int tiles_m, int tiles_n, int g
     int in_group = pid - group * per_group;
     tm = first_m + in_group % rows_here;
     tn = in_group / rows_here;
+}
+
+__device__ inline void tile_of(int pid, int num, int tiles_m, int tiles_n, int group_m,
+                               int& tm, int& tn) {
+    if ((num & 7) == 0) {
+        int per_xcd = num >> 3;
+        pid = (pid & 7) * per_xcd + (pid >> 3);
+    }
+    group_walk(pid, tiles_m, tiles_n, group_m, tm, tn);
 }
 
 // XOR swizzles of 16-byte chunks inside an LDS tile row.  The LDS-DMA copy
