@@ -61,7 +61,8 @@ enum Variant {
     V_PERSIST = 16,         // persistent 256x128 kernel for K = 128/256, 16-bit C stored during the next tile
     V_BT_256_K32_S4_AP = 17,  // B transposed: 256x256 tile, A in K-tile pairs, B^T in 4 32-wide stages
     V_SPLITK = 18,          // few output tiles: K split over the pipelined kernel's batch, + split-sum kernel
-    V_COUNT = 18
+    V_PERSIST_AP = 19,      // the persistent short-K kernel with A copied in K-tile pairs (whole lines)
+    V_COUNT = 19
 };
 
 bool is_bt_variant(int v) { return (v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2) || v == V_BT_256_K32_S4_AP; }
@@ -86,11 +87,12 @@ const char* const kVariantNames[] = {
     "persistent_256x128x32_shortk",
     "pipelined_bt_256x256x32_s4_apair",
     "splitk_pipelined",
+    "persistent_256x128x32_shortk_apair",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0, 4};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -463,8 +465,10 @@ int choose_pipelined(const Call& c) {
     // short K over many tiles (8 or more per CU): the persistent kernel
     // stores each tile's C during the next tile's K-loop; 64 x 4096^2 x 256
     // 1.17 -> 1.03 ms, K = 128 0.58 -> 0.49 ms on one machine, and even at 4
-    // tiles per CU it was 4% slower
-    if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return V_PERSIST;
+    // tiles per CU it was 4% slower.  A copied in K-tile pairs (whole
+    // 128-byte lines, half the A copy instructions): 64 x 4096^2 x 256
+    // 0.860 -> 0.810 ms against the half-line copies on one machine
+    if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return V_PERSIST_AP;
     // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
     // 1393 -> 1417 against the 32-wide 4-stage kernel on the same machine
     if (big && apair_ok(c)) return V_PIPE_256_K32_S4_AP;
@@ -673,7 +677,7 @@ hipError_t launch_apair(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename T, typename OutT>
+template <typename T, typename OutT, bool APAIR = false>
 hipError_t launch_persist(const Call& c, hipStream_t stream) {
     bpt::GemmArgs a;
     a.A = c.A; a.B = c.B; a.C = c.C;
@@ -687,10 +691,21 @@ hipError_t launch_persist(const Call& c, hipStream_t stream) {
     a.nb = (int)c.N;
     const int total = (int)((long long)a.tiles_m * a.tiles_n * c.batch);
     const int grid = total < 256 ? total : 256;            // one workgroup per CU
-    if (c.K == 256)
-        hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a, total);
-    else
-        hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a, total);
+    if constexpr (APAIR) {
+        if (c.K == 256)
+            hipLaunchKernelGGL((bpt::gemm_persist_apair_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(256), 0, stream,
+                               a, total);
+        else
+            hipLaunchKernelGGL((bpt::gemm_persist_apair_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(256), 0, stream,
+                               a, total);
+    } else {
+        if (c.K == 256)
+            hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+                               total);
+        else
+            hipLaunchKernelGGL((bpt::gemm_persist_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+                               total);
+    }
     return hipGetLastError();
 }
 
@@ -887,6 +902,9 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PERSIST:
             if constexpr (sizeof(OutT) == 2) return launch_persist<T, OutT>(c, stream);
             return hipErrorInvalidValue;                      // persist_ok: 16-bit C only
+        case V_PERSIST_AP:
+            if constexpr (sizeof(OutT) == 2) return launch_persist<T, OutT, true>(c, stream);
+            return hipErrorInvalidValue;
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -931,7 +949,8 @@ bool variant_accepts(const Call& c, int v) {
         case V_REPACK: return repack_feasible(c);
         case V_SPLITK: return splitk_splits(c) > 1;
         case V_PIPE_256_K32_S4_AP: return apair_ok(c);
-        case V_PERSIST: return persist_ok(c);
+        case V_PERSIST:
+        case V_PERSIST_AP: return persist_ok(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

@@ -136,7 +136,7 @@ def test_automatic_variant_choice():
     assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == apair
     assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == apair
     # short K over >= 2048 tiles of 256 x 128 (16-bit C): the persistent kernel
-    persist = v["persistent_256x128x32_shortk"]
+    persist = v["persistent_256x128x32_shortk_apair"]
     assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == persist
     assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == persist
     assert pkg.select_variant("f16", 4, 4096, 4096, 256, 256, 4096) == persist

@@ -55,6 +55,14 @@ def expected_waits(name):
         (nk,) = _ints(name)
         lps = (256 * 32 + 32 * 128) // 2048
         return {lps * 2 + lps // 2, lps * 2, 0}, lps * 2, nk
+    if base == "gemm_persist_apair_kernel":
+        # windows of 2 B copies (even K-tiles) or 2 B + 8 A-pair copies (odd);
+        # the publish after an even K-tile lets an even and an odd window
+        # fly, after an odd one only an even window; the prologue's lets an
+        # even window and half an odd one
+        (nk,) = _ints(name)
+        even, odd = 2, 2 + 8
+        return {even + odd // 2, even + odd, even, 0}, {even + odd, even}, nk
     if base == "gemm_skinny_ring_kernel":
         kc, s = _ints(name)[:2]
         lps = (64 * kc * 2) // 4096 + (kc * 128 * 2) // 4096
@@ -123,7 +131,7 @@ def check_publish_waits(kernels):
             assert m, f"{n}: barrier not preceded by a publish wait: {L[i - 1]!r}"
             seen.add(int(m.group(1)))
         assert seen <= allowed, f"{n}: wait counts {sorted(seen)} not in {sorted(allowed)}"
-        assert steady in seen, n
+        assert (steady <= seen) if isinstance(steady, set) else (steady in seen), n
         # the innermost loop around each barrier is the K-loop: per_iter
         # barriers, all with the steady count, no exec writes
         loops = _loops(L)
@@ -139,8 +147,10 @@ def check_publish_waits(kernels):
         for lp in k_loops:
             idx = sorted(i for i in lp if L[i] == "s_barrier")
             assert len(idx) == per_iter, f"{n}: {len(idx)} barriers per K-loop iteration, expected {per_iter}"
+            steady_set = steady if isinstance(steady, set) else {steady}
             for j in idx:
-                assert L[j - 1] == f"s_waitcnt vmcnt({steady}) lgkmcnt(0)", (n, L[j - 1])
+                m = re.match(r"s_waitcnt vmcnt\((\d+)\) lgkmcnt\(0\)$", L[j - 1])
+                assert m and int(m.group(1)) in steady_set, (n, L[j - 1])
             writes = [L[i] for i in sorted(lp) if _EXEC_WRITE.match(L[i])]
             assert not writes, f"{n}: the K-loop writes exec: {writes[:3]}"
 
@@ -196,7 +206,8 @@ def test_the_checks_catch_planted_mistakes(kernels):
         check_no_barrier_under_saved_exec(_planted(kernels, divergent))
 
 
-GEMM_TEMPLATES = ("gemm_pipelined_kernel", "gemm_apair_kernel", "gemm_persist_kernel", "gemm_skinny_kernel",
+GEMM_TEMPLATES = ("gemm_pipelined_kernel", "gemm_apair_kernel", "gemm_persist_kernel", "gemm_persist_apair_kernel",
+                  "gemm_skinny_kernel",
                   "gemm_skinny_ring_kernel", "gemm_generic_kernel", "skinny_sum_kernel", "splitk_sum_kernel",
                   "repack_pad_kernel", "fill_zero_kernel")
 
@@ -211,16 +222,16 @@ def test_gemm_kernels_use_no_scratch_and_spill_nothing(kernels):
         m = k["meta"]
         assert m["private_segment_fixed_size"] == 0, (n, m)
         assert m["vgpr_spill_count"] == 0, (n, m)
-        if base != "gemm_persist_kernel":       # its SGPRs: the test below
+        if base not in ("gemm_persist_kernel", "gemm_persist_apair_kernel"):   # their SGPRs: the test below
             assert m["sgpr_spill_count"] == 0, (n, m)
     assert seen == set(GEMM_TEMPLATES)
 
 
-@pytest.mark.xfail(strict=True, reason="the persistent short-K kernel still spills SGPRs into VGPR lanes "
-                                       "(v_writelane/v_readlane, no memory traffic)")
+@pytest.mark.xfail(strict=True, reason="the persistent short-K kernels still spill a few SGPRs into VGPR lanes "
+                                       "(v_writelane/v_readlane at the tile switch, no memory traffic)")
 def test_persistent_kernel_spills_no_sgpr(kernels):
     for n, k in kernels.items():
-        if asm_info.base_name(n) == "gemm_persist_kernel":
+        if asm_info.base_name(n) in ("gemm_persist_kernel", "gemm_persist_apair_kernel"):
             assert k["meta"]["sgpr_spill_count"] == 0, (n, k["meta"])
 
 

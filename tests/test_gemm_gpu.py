@@ -230,10 +230,14 @@ PERSIST_SHAPES = [("f16", 4, 1024, 2048, 256), ("f16", 6, 2048, 1024, 256), ("bf
                   ("f16", 32, 512, 1024, 256), ("f16", 6, 2048, 1024, 128), ("bf16", 4, 1024, 2048, 128)]
 
 
+PERSIST_VARIANTS = ["persistent_256x128x32_shortk", "persistent_256x128x32_shortk_apair"]
+
+
+@pytest.mark.parametrize("vname", PERSIST_VARIANTS)
 @pytest.mark.parametrize("dtype,batch,M,N,K", PERSIST_SHAPES)
-def test_persistent_parity(dtype, batch, M, N, K):
-    v = pkg.variants()["persistent_256x128x32_shortk"]
-    say(f"[persistent] {dtype} batch={batch} M={M} N={N} K={K}")
+def test_persistent_parity(dtype, batch, M, N, K, vname):
+    v = pkg.variants()[vname]
+    say(f"[persistent] {vname} {dtype} batch={batch} M={M} N={N} K={K}")
     A = inputs.uniform((batch, M, K), 7701 + M + N, dtype=dtype, nonzero=True)
     B = inputs.uniform((batch, K, N), 7702 + M + N, dtype=dtype, nonzero=True)
     check_random(A, B, dtype, False, v)
@@ -243,12 +247,13 @@ def test_persistent_parity(dtype, batch, M, N, K):
     assert np.array_equal(as_bits(got), oracle.encode(oracle.gemm(inputs.bits(Ai), inputs.bits(Bi), dtype), dtype))
 
 
+@pytest.mark.parametrize("vname", PERSIST_VARIANTS)
 @pytest.mark.parametrize("K", [256, 128])
-def test_persistent_padded_views_nan_padding(K):
+def test_persistent_padded_views_nan_padding(K, vname):
     """lda > K, ldb > N, ldc > N and batch strides from padded tensors, NaN
     in every padding element of A and B: the result must be correct and C's
     padding untouched."""
-    v = pkg.variants()["persistent_256x128x32_shortk"]
+    v = pkg.variants()[vname]
     b, M, N = 4, 1024, 2048                       # 256 tiles of 256 x 128
     say(f"[persistent padded] b={b} M={M} N={N} K={K}")
     A = inputs.uniform((b, M, K), 7721 + K, nonzero=True)
@@ -266,10 +271,11 @@ def test_persistent_padded_views_nan_padding(K):
     assert m["ok"], m
 
 
-def test_persistent_repeated_calls():
+@pytest.mark.parametrize("vname", PERSIST_VARIANTS)
+def test_persistent_repeated_calls(vname):
     """Back-to-back calls on one stream, the second into a C that the first
     filled: every call writes every tile once, bit-identical each time."""
-    v = pkg.variants()["persistent_256x128x32_shortk"]
+    v = pkg.variants()[vname]
     A = inputs.uniform((6, 2048, 256), 7711, nonzero=True).to(DEV)
     B = inputs.uniform((6, 256, 1024), 7712, nonzero=True).to(DEV)
     outs = [pkg.gemm_ex(A, B, variant=v) for _ in range(4)]
@@ -817,11 +823,13 @@ def test_persistent_schedule_matches_the_pipelined_kernel_bitwise():
     A = inputs.uniform((batch, M, K), 8501, nonzero=True).to(DEV)
     B = inputs.uniform((batch, K, N), 8502, nonzero=True).to(DEV)
     p = pkg.gemm_ex(A, B, variant=V["persistent_256x128x32_shortk"])
+    pa = pkg.gemm_ex(A, B, variant=V["persistent_256x128x32_shortk_apair"])
     q = pkg.gemm_ex(A, B, variant=V["pipelined_256x256x32_s4"])
     r = pkg.gemm_ex(A, B, variant=V["pipelined_128x128x32_s4"])
     torch.cuda.synchronize()
     assert torch.equal(p.cpu().view(torch.int16), q.cpu().view(torch.int16))
     assert torch.equal(p.cpu().view(torch.int16), r.cpu().view(torch.int16))
+    assert torch.equal(pa.cpu().view(torch.int16), q.cpu().view(torch.int16))
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (96, 8192, 2048), (65, 1000, 1024), (64, 512, 65536),
@@ -877,7 +885,7 @@ def test_operand_over_2gib_runs_on_64bit_offsets():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("out_fp32,vname", [(False, "persistent_256x128x32_shortk"),
+@pytest.mark.parametrize("out_fp32,vname", [(False, "persistent_256x128x32_shortk_apair"),
                                             (True, "pipelined_256x256x32_s4_apair")])
 def test_single_output_over_2gib(out_fp32, vname):
     """One C of 32768 x 32768 (2 GiB in fp16, 4 GiB in fp32) from the fast
