@@ -1079,6 +1079,9 @@ struct AttnCall {
 // 1.03 ms with (8, 32, 4) against 1.24 ms with (4, 64, 2) (32-key blocks keep
 // a wave within the 256 registers two waves per SIMD leave; (8, 64, 2) spills
 // and took 1.78 ms); D = 128 at 0.539 ms with (8, 64, 2) against 0.557 ms.
+// Shifting the two waves of a SIMD half a block apart (a stage refilled two
+// blocks after its use, one stage more) measured slower: D = 256 1.003 ms
+// against 0.967 with the waves in step, D = 128 0.542 against 0.513.
 constexpr int kAttnWaves256 = 8, kAttnBlock256 = 32, kAttnStages256 = 4;
 constexpr int kAttnWaves128 = 8, kAttnBlock128 = 64, kAttnStages128 = 2;
 

@@ -14,15 +14,17 @@
 //   and keeps its Q fragments in registers for the whole key loop.  Every
 //   softmax statistic of a row lives in that row's two lanes (l and l+32),
 //   so no reduction crosses waves -- the pages' barrier for the shared
-//   softmax maximum has nothing to do here.  With 8 waves, two share each
-//   SIMD: while one runs its softmax on the vector unit, the other's matrix
-//   products keep the matrix core busy (a wave alone leaves it idle through
-//   its softmax).  That needs a wave to fit in 256 registers, which at head
-//   dimension 256 holds for 32-key blocks.
+//   softmax maximum has nothing to do here.  Two waves share each SIMD
+//   (waves w and w + WAVES/2), which needs a wave to fit in 256 registers;
+//   at head dimension 256 that holds for 32-key blocks.
 // * K and V blocks of BN keys are staged global->LDS by LDS-DMA in a ring of
 //   STAGES stages.  Block j is published by a vmcnt wait plus one s_barrier;
 //   right after it the copies of block j+STAGES-1 are issued into the stage
 //   block j-1 left (the window), and the math of block j follows.
+// * The K and V fragments for the matrix products are read from LDS two
+//   MFMAs ahead of their use.  With both fragment reads and the O and Q
+//   registers a wave holds, the compiler otherwise kept one fragment in
+//   flight and waited for each read right before its MFMA.
 // * S never goes through LDS.  S^T = K Q^T is formed with K as the MFMA's
 //   row operand, so lane l holds query row l%32 and 16 keys of each 32 keys
 //   of a block.  Those are exactly the keys its half of the wave must supply
@@ -175,41 +177,56 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         };
 
         // fragment reads.  K (row operand of S^T = K Q^T): key 32kb + l%32,
-        // logical chunk 2t + h, physical (2t + h) ^ (l & 15); the XOR keeps
-        // bit 4, so t >= 8 adds 256 bytes.
-        uint32_t rdK[8];
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
-            rdK[t8] = (uint32_t)((lane & 31) * D * 2 + (((2 * t8 + h) ^ attn_swz_k(lane)) * 16));
+        // logical chunk 2t + h, physical (2t + h) ^ (l & 15).  2t and h are
+        // disjoint bits, so the physical chunk is 2t ^ y with y = h ^ (l & 15),
+        // and the byte address row + 16 (2t ^ y) = (row + 16 y) ^ 32t: one
+        // base register and one XOR per read (stage and kb offsets lie above
+        // the XOR's bits).
+        const uint32_t kbase = (uint32_t)((lane & 31) * D * 2 + 16 * (h ^ attn_swz_k(lane)));
         // V (row operand of O^T = V^T P^T), transposing 4-row reads: 16-lane
         // group g, lane j reads row 4(g/2) + j/4 (+8 for the upper four keys,
         // +16ks) at columns 32db + 16(g%2) + 4(j%4); chunk 4db + x with
         // x = 2(g%2) + (j%4)/2, swizzled by s = swz_b(j/4):
-        // (4db + x) ^ s = 4(db ^ (s>>2)) + (x ^ (s&3)).
+        // (4db + x) ^ s = 4(db ^ (s>>2)) + (x ^ (s&3)).  The byte address is
+        // vbase ^ 64(db & 3), plus 256 for db >= 4.
         const int g = lane >> 4, jj = lane & 15;
         const int sv = swz_b(jj >> 2);
         const int xv = 2 * (g & 1) + ((jj & 3) >> 1);
-        uint32_t rdV[4];
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4)
-            rdV[w4] = (uint32_t)((4 * (g >> 1) + (jj >> 2)) * D * 2 + 64 * (w4 ^ (sv >> 2)) +
-                                 16 * (xv ^ (sv & 3)) + 8 * (jj & 1));
+        const uint32_t vbase = (uint32_t)((4 * (g >> 1) + (jj >> 2)) * D * 2 + 64 * (sv >> 2) +
+                                          16 * (xv ^ (sv & 3)) + 8 * (jj & 1));
 
-        auto block = [&]<bool MASK>(int j) __attribute__((always_inline)) {
-            BPT_LDS char* kt = lds + (j & (STAGES - 1)) * G::STAGE;
-            BPT_LDS char* vt = kt + G::TILE;
-            // S^T for keys BN j .. BN j + BN-1 (KB 32-key halves)
-            float16_t s[G::KB];
+        // S^T for keys BN j .. BN j + BN-1 (KB 32-key halves)
+        // Each fragment read goes out PD MFMAs ahead of its use, so its
+        // latency runs under earlier MFMAs instead of stalling the wave.  The
+        // scheduling fences keep that order (without the one before the
+        // MFMA, the compiler moved the read below it).
+        constexpr int PD = 2;
+        auto qk = [&](int j, float16_t (&s)[G::KB]) __attribute__((always_inline)) {
+            const uint32_t kj = kbase + (uint32_t)((j & (STAGES - 1)) * G::STAGE);
+            constexpr int N = TS * G::KB;
+            auto kread = [&](int i) __attribute__((always_inline)) {
+                const int t = i / G::KB, kb = i % G::KB;
+                return *(BPT_LDS frag_t*)(lds + (kj ^ (32u * t)) + kb * 32 * D * 2);
+            };
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
                 s[kb] = float16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            frag_t kf[PD + 1];
 #pragma unroll
-            for (int t = 0; t < TS; ++t)
+            for (int i = 0; i < PD; ++i) kf[i] = kread(i);
 #pragma unroll
-                for (int kb = 0; kb < G::KB; ++kb) {
-                    frag_t kf = *(BPT_LDS frag_t*)(kt + rdK[t & 7] + (t >> 3) * 256 + kb * 32 * D * 2);
-                    s[kb] = Mfma<T>::mma32(kf, qf[t], s[kb]);
-                }
+            for (int i = 0; i < N; ++i) {
+                if (i + PD < N) kf[(i + PD) % (PD + 1)] = kread(i + PD);
+                __builtin_amdgcn_sched_barrier(0);
+                const int t = i / G::KB, kb = i % G::KB;
+                s[kb] = Mfma<T>::mma32(kf[i % (PD + 1)], qf[t], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // the online softmax of block j: running max, rescale of O and the
+        // row sum, and the weights P as PV operands
+        auto softmax = [&]<bool MASK>(int j, const float16_t (&s)[G::KB], frag_t (&pf)[G::PVS])
+            __attribute__((always_inline)) {
             // the row maximum of the logits in base 2, from the raw products
             // (the scale is monotone; keys >= Skv excluded when MASK); register
             // r of half kb holds key BN j + 32kb + 8(r/4) + 4h + r%4
@@ -251,7 +268,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
             // block are registers 8(ks&1) .. +7 of half ks>>1); the row sum
             // adds the rounded weights, the values the PV product uses
             const float nmref = m_run == kNegInf ? 0.f : -m_run;
-            frag_t pf[G::PVS];
 #pragma unroll
             for (int ks = 0; ks < G::PVS; ++ks)
 #pragma unroll
@@ -266,17 +282,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
 #pragma unroll
                 for (int i = 0; i < 4; ++i) psum = Mfma<T>::dot2(pf[ks][2 * i], pf[ks][2 * i + 1], psum);
             l_half = psum;
-            // O^T += V^T P^T
+        };
+        // O^T += V^T P^T for block j
+        auto pv = [&](int j, const frag_t (&pf)[G::PVS]) __attribute__((always_inline)) {
+            const uint32_t vj = vbase + (uint32_t)((j & (STAGES - 1)) * G::STAGE + G::TILE);
+            constexpr int N = G::PVS * DB;
+            auto vread = [&](int i) __attribute__((always_inline)) {
+                const int ks = i / DB, db = i % DB;
+                BPT_LDS char* p = lds + (vj ^ (64u * (db & 3))) + (db >> 2) * 256 + ks * 16 * D * 2;
+                short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
+                short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 8 * D * 2));
+                return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            frag_t vf[PD + 1];
 #pragma unroll
-            for (int ks = 0; ks < G::PVS; ++ks)
+            for (int i = 0; i < PD; ++i) vf[i] = vread(i);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    BPT_LDS char* p = vt + rdV[db & 3] + (db >> 2) * 256 + ks * 16 * D * 2;
-                    short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)p);
-                    short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BPT_LDS short4_t*)(p + 8 * D * 2));
-                    frag_t vf = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = Mfma<T>::mma32(vf, pf[ks], oacc[db]);
-                }
+            for (int i = 0; i < N; ++i) {
+                if (i + PD < N) vf[(i + PD) % (PD + 1)] = vread(i + PD);
+                __builtin_amdgcn_sched_barrier(0);
+                const int ks = i / DB, db = i % DB;
+                oacc[db] = Mfma<T>::mma32(vf[i % (PD + 1)], pf[ks], oacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
 
         // Ring of STAGES: blocks 0 .. STAGES-2 are copied ahead; step j
@@ -294,24 +322,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         for (int b = 0; b < STAGES - 1; ++b) issue(b);
         // host: RAGGED == (Skv % BN != 0)
         const int nfull = RAGGED ? nblk - 1 : nblk;
+        float16_t s[G::KB];
+        frag_t pf[G::PVS];
         int j = 0;
         for (; j < nfull; ++j) {
             publish();
             issue(j + STAGES - 1);
-            block.template operator()<false>(j);
+            qk(j, s);
+            softmax.template operator()<false>(j, s, pf);
+            pv(j, pf);
         }
         if constexpr (RAGGED) {
             publish();
-            block.template operator()<true>(j);
+            qk(j, s);
+            softmax.template operator()<true>(j, s, pf);
+            pv(j, pf);
         }
         // no copy may still be writing LDS when the workgroup ends
         wait_vm<0>();
     }
 
     // ---- O = O / l, rows < Sq ------------------------------------------------
+    // the lane number read afresh: kept from the start, it and its half
+    // would hold two registers through the key loop, which at D = 256 has
+    // none to spare (the compiler spilled them)
+    int lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+    const int he = lane_e >> 5;
     const float l_row = l_half + __shfl_xor(l_half, 32);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int qrow = q0 + wave * 32 + (lane & 31);
+    const int qrow = q0 + wave * 32 + (lane_e & 31);
     if (qrow < Sq) {
         OutT* orow = static_cast<OutT*>(a.O) + bh * a.sO + (long long)qrow * a.ldo;
         typedef OutT out4_t __attribute__((ext_vector_type(4)));
@@ -324,7 +364,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
                 for (int q = 0; q < 4; ++q) v[q] = cvt_out<OutT>(oacc[db][4 * r4 + q] * inv);
                 // plain stores: each lane writes 8-byte pieces of its row, which
                 // the L2 merges (non-temporal stores measured 2% slower here)
-                *(out4_t*)(orow + 32 * db + 8 * r4 + 4 * h) = v;
+                *(out4_t*)(orow + 32 * db + 8 * r4 + 4 * he) = v;
             }
     }
 }

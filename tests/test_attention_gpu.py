@@ -47,10 +47,12 @@ def check_random(q, k, v, scale, dtype, out_fp32):
     return m
 
 
-# (BH, Sq, Skv, D): whole and ragged query tiles (128 rows) and key blocks
-# (64 keys), one query or key, several key blocks with a ragged tail
+# (BH, Sq, Skv, D): whole and ragged query tiles (256 rows) and key blocks
+# (32 keys at D = 256, 64 at D = 128), one query or key, exactly one whole
+# key block (the second half of the waves runs only its first, peeled
+# block), several key blocks with a ragged tail
 SHAPES = [(1, 128, 64, 256), (2, 300, 200, 256), (1, 1, 1, 256), (3, 129, 1000, 128), (2, 257, 63, 128),
-          (1, 64, 4096, 256), (4, 128, 130, 256)]
+          (1, 64, 4096, 256), (4, 128, 130, 256), (2, 256, 32, 256), (1, 300, 64, 128)]
 
 
 @pytest.mark.parametrize("BH,Sq,Skv,D", SHAPES)
