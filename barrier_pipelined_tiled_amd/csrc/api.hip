@@ -19,6 +19,7 @@
 #include "attention.hpp"
 #include "gemm_apair.hpp"
 #include "gemm_persist.hpp"
+#include "gemm_persist_ares.hpp"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
@@ -62,7 +63,8 @@ enum Variant {
     V_BT_256_K32_S4_AP = 17,  // B transposed: 256x256 tile, A in K-tile pairs, B^T in 4 32-wide stages
     V_SPLITK = 18,          // few output tiles: K split over the pipelined kernel's batch, + split-sum kernel
     V_PERSIST_AP = 19,      // the persistent short-K kernel with A copied in K-tile pairs (whole lines)
-    V_COUNT = 19
+    V_PERSIST_AR = 20,      // the persistent short-K kernel walking row blocks with their A panel kept in LDS
+    V_COUNT = 20
 };
 
 bool is_bt_variant(int v) { return (v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2) || v == V_BT_256_K32_S4_AP; }
@@ -88,11 +90,12 @@ const char* const kVariantNames[] = {
     "pipelined_bt_256x256x32_s4_apair",
     "splitk_pipelined",
     "persistent_256x128x32_shortk_apair",
+    "persistent_256x128x32_shortk_aresident",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0, 4};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0, 32, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0, 4, 3};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -468,7 +471,10 @@ int choose_pipelined(const Call& c) {
     // tiles per CU it was 4% slower.  A copied in K-tile pairs (whole
     // 128-byte lines, half the A copy instructions): 64 x 4096^2 x 256
     // 0.860 -> 0.810 ms against the half-line copies on one machine
-    if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return V_PERSIST_AP;
+    // With K = 128 the kernel that keeps each row block's A panel in LDS and
+    // streams only B: 64 x 4096^2 x 128 0.493 -> 0.466 ms; with K = 256 its
+    // 3-stage ring leaves the stores no room and it is slower (0.90 ms)
+    if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return c.K == 128 ? V_PERSIST_AR : V_PERSIST_AP;
     // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
     // 1393 -> 1417 against the 32-wide 4-stage kernel on the same machine
     if (big && apair_ok(c)) return V_PIPE_256_K32_S4_AP;
@@ -709,6 +715,38 @@ hipError_t launch_persist(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The A-resident persistent kernel walks groups of gn column tiles of one
+// row block.  The columns of a row block are split into nsplit ranges, the
+// largest power of two with tiles_m * nsplit <= 32 that divides tiles_n:
+// then the 32 workgroups of one XCD hold the groups of about one batch
+// entry at a time (16 row blocks x 2 ranges for 4096 x 4096), and its L2
+// holds that entry's B once.
+template <typename T, typename OutT>
+hipError_t launch_persist_ares(const Call& c, hipStream_t stream) {
+    bpt::GemmArgs a;
+    a.A = c.A; a.B = c.B; a.C = c.C;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_m = (int)(c.M / 256);
+    a.tiles_n = (int)(c.N / 128);
+    a.group_m = 1;
+    a.c_vec = 1;
+    a.nb = (int)c.N;
+    int nsplit = 1;
+    while (nsplit * 2 * a.tiles_m <= 32 && a.tiles_n % (nsplit * 2) == 0) nsplit *= 2;
+    const int gn = a.tiles_n / nsplit;
+    const int ngroups = (int)((long long)a.tiles_m * nsplit * c.batch);
+    const int grid = ngroups < 256 ? ngroups : 256;        // one workgroup per CU
+    if (c.K == 256)
+        hipLaunchKernelGGL((bpt::gemm_persist_ares_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+                           ngroups, gn, nsplit);
+    else
+        hipLaunchKernelGGL((bpt::gemm_persist_ares_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+                           ngroups, gn, nsplit);
+    return hipGetLastError();
+}
+
 template <typename T, typename OutT>
 hipError_t launch_skinny(const Call& c, hipStream_t stream) {
     bpt::SkinnyArgs a;
@@ -905,6 +943,9 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PERSIST_AP:
             if constexpr (sizeof(OutT) == 2) return launch_persist<T, OutT, true>(c, stream);
             return hipErrorInvalidValue;
+        case V_PERSIST_AR:
+            if constexpr (sizeof(OutT) == 2) return launch_persist_ares<T, OutT>(c, stream);
+            return hipErrorInvalidValue;
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -950,7 +991,8 @@ bool variant_accepts(const Call& c, int v) {
         case V_SPLITK: return splitk_splits(c) > 1;
         case V_PIPE_256_K32_S4_AP: return apair_ok(c);
         case V_PERSIST:
-        case V_PERSIST_AP: return persist_ok(c);
+        case V_PERSIST_AP:
+        case V_PERSIST_AR: return persist_ok(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

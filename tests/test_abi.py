@@ -138,7 +138,8 @@ def test_automatic_variant_choice():
     # short K over >= 2048 tiles of 256 x 128 (16-bit C): the persistent kernel
     persist = v["persistent_256x128x32_shortk_apair"]
     assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == persist
-    assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == persist
+    # K = 128: the kernel keeping each row block's A panel in LDS
+    assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == v["persistent_256x128x32_shortk_aresident"]
     assert pkg.select_variant("f16", 4, 4096, 4096, 256, 256, 4096) == persist
     assert pkg.select_variant("f16", 2, 4096, 4096, 256, 256, 4096) == apair      # 1024 tiles
     assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096, True) == apair   # fp32 C

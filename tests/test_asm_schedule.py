@@ -63,6 +63,13 @@ def expected_waits(name):
         (nk,) = _ints(name)
         even, odd = 2, 2 + 8
         return {even + odd // 2, even + odd, even, 0}, {even + odd, even}, nk
+    if base == "gemm_persist_ares_kernel":
+        # 3 B stages of 2 copies per wave at K = 256, 4 at K = 128: publish
+        # lets BSTAGES-2 windows fly, the prologue's half a window more; a
+        # new group's panel sits between two full publishes in the loop body
+        (nk,) = _ints(name)
+        vm = 2 * ((3 if nk == 8 else 4) - 2)
+        return {vm + 1, vm, 0}, {vm, 0}, nk + 2
     if base == "gemm_skinny_ring_kernel":
         kc, s = _ints(name)[:2]
         lps = (64 * kc * 2) // 4096 + (kc * 128 * 2) // 4096
@@ -207,7 +214,7 @@ def test_the_checks_catch_planted_mistakes(kernels):
 
 
 GEMM_TEMPLATES = ("gemm_pipelined_kernel", "gemm_apair_kernel", "gemm_persist_kernel", "gemm_persist_apair_kernel",
-                  "gemm_skinny_kernel",
+                  "gemm_persist_ares_kernel", "gemm_skinny_kernel",
                   "gemm_skinny_ring_kernel", "gemm_generic_kernel", "skinny_sum_kernel", "splitk_sum_kernel",
                   "repack_pad_kernel", "fill_zero_kernel")
 
@@ -222,7 +229,7 @@ def test_gemm_kernels_use_no_scratch_and_spill_nothing(kernels):
         m = k["meta"]
         assert m["private_segment_fixed_size"] == 0, (n, m)
         assert m["vgpr_spill_count"] == 0, (n, m)
-        if base not in ("gemm_persist_kernel", "gemm_persist_apair_kernel"):   # their SGPRs: the test below
+        if base not in ("gemm_persist_kernel", "gemm_persist_apair_kernel", "gemm_persist_ares_kernel"):   # SGPRs: below
             assert m["sgpr_spill_count"] == 0, (n, m)
     assert seen == set(GEMM_TEMPLATES)
 
@@ -231,7 +238,7 @@ def test_gemm_kernels_use_no_scratch_and_spill_nothing(kernels):
                                        "(v_writelane/v_readlane at the tile switch, no memory traffic)")
 def test_persistent_kernel_spills_no_sgpr(kernels):
     for n, k in kernels.items():
-        if asm_info.base_name(n) in ("gemm_persist_kernel", "gemm_persist_apair_kernel"):
+        if asm_info.base_name(n) in ("gemm_persist_kernel", "gemm_persist_apair_kernel", "gemm_persist_ares_kernel"):
             assert k["meta"]["sgpr_spill_count"] == 0, (n, k["meta"])
 
 

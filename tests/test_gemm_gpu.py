@@ -230,7 +230,8 @@ PERSIST_SHAPES = [("f16", 4, 1024, 2048, 256), ("f16", 6, 2048, 1024, 256), ("bf
                   ("f16", 32, 512, 1024, 256), ("f16", 6, 2048, 1024, 128), ("bf16", 4, 1024, 2048, 128)]
 
 
-PERSIST_VARIANTS = ["persistent_256x128x32_shortk", "persistent_256x128x32_shortk_apair"]
+PERSIST_VARIANTS = ["persistent_256x128x32_shortk", "persistent_256x128x32_shortk_apair",
+                    "persistent_256x128x32_shortk_aresident"]
 
 
 @pytest.mark.parametrize("vname", PERSIST_VARIANTS)
@@ -830,6 +831,37 @@ def test_persistent_schedule_matches_the_pipelined_kernel_bitwise():
     assert torch.equal(p.cpu().view(torch.int16), q.cpu().view(torch.int16))
     assert torch.equal(p.cpu().view(torch.int16), r.cpu().view(torch.int16))
     assert torch.equal(pa.cpu().view(torch.int16), q.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("K", [256, 128])
+def test_resident_panel_kernel_over_several_groups(K):
+    """The A-resident persistent kernel where each workgroup walks two row
+    blocks' groups of 4 column tiles (16 x 2048 x 2048: 8 row blocks, the
+    16 column tiles split in 4 ranges, 512 groups on 256 workgroups), so the
+    panel is reloaded mid-walk: bitwise equal to the A-pair persistent
+    kernel (same products in the same order), sampled outputs within the
+    oracle's bound, and integer inputs exact everywhere sampled."""
+    V = pkg.variants()
+    b, M, N = 16, 2048, 2048
+    say(f"[persistent groups] b={b} M={M} N={N} K={K}")
+    A = inputs.uniform((b, M, K), 8601 + K, nonzero=True)
+    B = inputs.uniform((b, K, N), 8602 + K, nonzero=True)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    r = pkg.gemm_ex(Ad, Bd, variant=V["persistent_256x128x32_shortk_aresident"])
+    q = pkg.gemm_ex(Ad, Bd, variant=V["persistent_256x128x32_shortk_apair"])
+    torch.cuda.synchronize()
+    assert torch.equal(r.view(torch.int16), q.view(torch.int16))
+    for e in (0, 7, 15):
+        got, ref = _sampled_block(A[e], B[e], r[e], 8603 + e)
+        m = oracle.compare(got.float().numpy(), ref, K)
+        assert m["ok"], (e, m)
+    Ai = inputs.small_integers((b, M, K), 8611)
+    Bi = inputs.small_integers((b, K, N), 8612)
+    ri = pkg.gemm_ex(Ai.to(DEV), Bi.to(DEV), variant=V["persistent_256x128x32_shortk_aresident"])
+    torch.cuda.synchronize()
+    for e in (0, 9):
+        got, ref = _sampled_block(Ai[e], Bi[e], ri[e], 8613 + e)
+        assert np.array_equal(as_bits(got), oracle.encode(ref, "f16")), e
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (96, 8192, 2048), (65, 1000, 1024), (64, 512, 65536),
