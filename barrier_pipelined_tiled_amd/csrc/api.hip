@@ -364,7 +364,14 @@ WsLease ws_acquire(long long bytes, hipStream_t stream) {
     if (grow || s->ptr == nullptr) {
         void* p = nullptr;
         const long long want = ws_size_for(bytes, s->bytes);
-        if (hipMalloc(&p, (size_t)want) != hipSuccess) {
+        // relaxed capture mode for this thread around the allocation: in the
+        // default (global) mode, an allocation while another thread captures
+        // a stream in global mode could invalidate that capture
+        hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+        const bool swapped = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess;
+        const hipError_t e = hipMalloc(&p, (size_t)want);
+        if (swapped) (void)hipThreadExchangeStreamCaptureMode(&mode);
+        if (e != hipSuccess) {
             (void)hipGetLastError();
             return L;                    // the call runs without a workspace
         }
@@ -871,7 +878,7 @@ void launch_repack_copy(const void* src, long long ld, long long stride, void* d
 }
 
 // Split-K for few output tiles: the K ranges run as one batched call of a
-// pipelined variant into fp32 partials in the stream's workspace, then the
+// pipelined variant into fp32 partials in the call's workspace, then the
 // in-order sum kernel writes C.  Without a workspace the call runs unsplit.
 template <typename T, typename OutT>
 hipError_t launch_splitk(const Call& c, hipStream_t stream) {
