@@ -557,7 +557,7 @@ bool repack_ok(const Call& c) {
 // An output of at most 128 tiles of 128 x 128 (fewer than half the CUs get
 // a workgroup) is computed as S K-ranges at once: the pipelined kernel runs
 // with the ranges as its batch (A advanced by K/S columns, B by K/S rows per
-// entry) into fp32 partials in the stream's workspace, and splitk_sum_kernel
+// entry) into fp32 partials in the call's workspace, and splitk_sum_kernel
 // adds them in split order.  S is the largest power of two (at most 64) that
 // keeps the tiles within one workgroup per CU, with K/S a multiple of 64 and
 // at least 256.  With B given transposed, entry s reads Bt from column
@@ -905,7 +905,7 @@ hipError_t launch_splitk(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Copy A and B into the stream's workspace, zero-padded and aligned, then run
+// Copy A and B into the call's workspace, zero-padded and aligned, then run
 // the pipelined kernel on the copies.  Without a workspace (graph capture,
 // allocation failure) the guarded kernel takes the call as it is.
 template <typename T, typename OutT>

@@ -3,7 +3,7 @@
 // A call whose output has too few tiles to give every CU a workgroup runs
 // the pipelined kernel once over S K-ranges at a time, each range as one
 // entry of the kernel's batch, writing an fp32 partial product per range
-// into the stream's workspace ([split][M][N], rows of N).  This kernel then
+// into the call's workspace ([split][M][N], rows of N).  This kernel then
 // adds the S partials of every output in split order (so the result does
 // not depend on timing) and stores C, converted with round-to-nearest-even.
 // (Split-K itself is not on the pages: their GEMM fills the GPU with output

@@ -461,6 +461,8 @@ def main():
                          "starts at the steady clock (0: none; the first --steps steps after the "
                          "pause are then the timed block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads for the oracle's CPU baseline (0: all the host offers)")
     ap.add_argument("--no-clocks", action="store_true", help="skip the amd-smi clock and power readings")
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
                     help="GEMM only.  kn: B is K x N (the workloads' layout); nt: the same B handed "
@@ -506,6 +508,9 @@ def main():
     roof = roofline(w.flops, w.compulsory_bytes, kernel_ms)
     roof["traffic"] = measured_traffic(w.name, kernel)
     config["pct_of_dense_peak"] = 100.0 * value / PEAK_MFMA_F16_TFLOPS
+    if args.cpu_threads > 0 and not args.no_cpu_baseline:
+        import oracle
+        oracle.set_num_threads(args.cpu_threads)
     cpu = None if args.no_cpu_baseline else baseline()
 
     out = {

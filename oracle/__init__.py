@@ -72,6 +72,8 @@ def _load():
                                      ctypes.c_double, i64, p, p, p, p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -82,6 +84,12 @@ _DTYPES = {"f16": 0, "bf16": 1}
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Run the oracle's parallel loops on n threads (results do not depend
+    on n: each output element is summed by one thread, in ascending k)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------

@@ -329,3 +329,10 @@ int oracle_num_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Set that number (n >= 1); the results do not depend on it, since every
+ * output element is summed by one thread in its fixed order. */
+void oracle_set_num_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}

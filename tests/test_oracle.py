@@ -301,6 +301,24 @@ def test_batched_equals_single_calls():
         assert np.array_equal(c[b], oracle.gemm(A[b], B[b]))
 
 
+def test_thread_count_changes_nothing():
+    """One thread and all of them give the same bits (each output element
+    is one thread's ascending-k sum), and the setter takes effect."""
+    rng = np.random.default_rng(20)
+    A = f16_bits(rng.uniform(-1, 1, size=(2, 70, 130)))
+    B = f16_bits(rng.uniform(-1, 1, size=(2, 130, 45)))
+    n0 = oracle.num_threads()
+    try:
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        one32, one64 = oracle.gemm(A, B, want64=True)
+    finally:
+        oracle.set_num_threads(n0)
+    assert oracle.num_threads() == n0
+    all32, all64 = oracle.gemm(A, B, want64=True)
+    assert np.array_equal(one32, all32) and np.array_equal(one64, all64)
+
+
 def test_gemm_at_equals_full_product():
     rng = np.random.default_rng(19)
     for dtype in ("f16", "bf16"):
