@@ -309,7 +309,7 @@ def test_repeat_runs_bitwise_identical():
 @pytest.mark.parametrize("M,N,K,vname", [(64, 2048, 4096, "skinny_64x128_ring_k32_s4_splitk"),   # 16 splits eager
                                          (256, 2048, 4096, "splitk_pipelined")])                # 8 splits eager
 def test_graph_capture_of_a_split_k_call(M, N, K, vname):
-    """A call captured into a graph must not use the per-stream workspace (a
+    """A call captured into a graph takes no buffer from the workspace pool (a
     graph would keep its address): captured, the split-K paths run unsplit.
     Exact-integer inputs make the split (eager) and unsplit (captured) sums
     bit-identical, so every replay -- with eager calls and synchronisations

@@ -83,3 +83,41 @@ def test_noalloc_exact_integers_repeated():
     torch.cuda.synchronize()
     for j, C in outs:
         assert np.array_equal(C.cpu().numpy(), data[j][2])
+
+
+@pytest.mark.parametrize("M,N,K,vname", [(64, 8192, 8192, "skinny_64x128_ring_k32_s4_splitk"),
+                                         (1024, 1024, 8192, "splitk_pipelined")])
+def test_noalloc_under_graph_capture_keeps_its_splits(M, N, K, vname):
+    """Captured into a graph, gemm_ex_noalloc still runs its split paths
+    (gemm_ex, which takes no pool buffer under capture, runs unsplit): the
+    same kernels and split counts as the eager gemm_ex call, so each of three
+    replays -- with eager calls and synchronisations between them -- equals
+    that call bit for bit, and (integer inputs) the oracle exactly."""
+    assert pkg.select_variant("f16", 1, M, N, K, K, N, True) == pkg.variants()[vname]
+    print(f"noalloc capture {vname} M={M} N={N} K={K}", flush=True)
+    A = inputs.small_integers((M, K), 9301)
+    B = inputs.small_integers((K, N), 9302)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(B), "f16")
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    eager = pkg.gemm_ex(Ad, Bd, out_fp32=True)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                 # warm-up on a side stream, as torch advises
+        pkg.gemm_ex_noalloc(Ad, Bd, C, out_fp32=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(eager.cpu().numpy(), ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkg.gemm_ex_noalloc(Ad, Bd, C, out_fp32=True)
+    for rep in range(3):
+        C.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, eager), rep
+        again = pkg.gemm_ex(Ad, Bd, out_fp32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager), rep
+    assert np.array_equal(C.cpu().numpy(), ref)
