@@ -225,9 +225,12 @@ def test_batched_small(vname):
 
 # the persistent short-K kernel: whole 256 x 128 tiles, K = 128 or 256,
 # 16-bit C, at least 256 tiles.  Tile counts 256, 384 (some workgroups walk
-# two tiles, some one), 512, and 512 over 32 batch entries.
+# two tiles, some one), 512, and 512 over 32 batch entries; 400 tiles of 5
+# row blocks, which the A-resident kernel walks as 100 groups of 4 on a grid
+# of 100 (not a multiple of 8: the plain round-robin walk).
 PERSIST_SHAPES = [("f16", 4, 1024, 2048, 256), ("f16", 6, 2048, 1024, 256), ("bf16", 1, 4096, 4096, 256),
-                  ("f16", 32, 512, 1024, 256), ("f16", 6, 2048, 1024, 128), ("bf16", 4, 1024, 2048, 128)]
+                  ("f16", 32, 512, 1024, 256), ("f16", 6, 2048, 1024, 128), ("bf16", 4, 1024, 2048, 128),
+                  ("f16", 5, 1280, 2048, 256)]
 
 
 PERSIST_VARIANTS = ["persistent_256x128x32_shortk", "persistent_256x128x32_shortk_apair",
