@@ -241,7 +241,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
                     const float x = masked(kb, r) ? kFar : s[kb][r];
                     mraw = POS ? __builtin_fmaxf(mraw, x) : __builtin_fminf(mraw, x);
                 }
-            mraw = POS ? __builtin_fmaxf(mraw, __shfl_xor(mraw, 32)) : __builtin_fminf(mraw, __shfl_xor(mraw, 32));
+            // join the row's two lanes (l and l+32): v_permlane32_swap of the
+            // value with itself leaves the lower half's values in one result
+            // and the upper half's in the other, in every lane, and max/min
+            // of the two is the row's in both halves -- no LDS round trip
+            // (a shuffle through ds_bpermute sat on the softmax's critical
+            // path)
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mraw),
+                                                                 __builtin_bit_cast(unsigned, mraw), false, false);
+                const float lo = __builtin_bit_cast(float, (unsigned)sw[0]);
+                const float hi = __builtin_bit_cast(float, (unsigned)sw[1]);
+                mraw = POS ? __builtin_fmaxf(lo, hi) : __builtin_fminf(lo, hi);
+            }
             const float mloc = mraw * a.c2;
             // raise the running max only when some row would otherwise see a
             // weight above 2^8
