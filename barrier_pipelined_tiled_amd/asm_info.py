@@ -103,11 +103,11 @@ def template_hash(hashes: dict, base: str) -> str | None:
 _BRANCH = re.compile(r"^s_(cbranch_\w+|branch) (\.LBB_\d+)$")
 
 
-def natural_loops(lines: list) -> list:
-    """The loops of a kernel's control flow: for every back edge (a branch to
-    a block that dominates it) the set of line indices of the loop's blocks.
-    Built from basic blocks (split at labels and after branches), so a
-    backward jump that only reflects block placement is not a loop."""
+def basic_blocks(lines: list) -> tuple:
+    """A kernel's basic blocks (split at labels and after branches and
+    s_endpgm): their first line indices, their end indices (exclusive) and
+    each block's successors (branch target, and the next block unless the
+    block ends in an unconditional branch or s_endpgm)."""
     starts = [0]
     for i, l in enumerate(lines):
         if l.endswith(":") and i != 0:
@@ -131,6 +131,15 @@ def natural_loops(lines: list) -> list:
                 succ[b].append(b + 1)
         elif last != "s_endpgm" and b + 1 < len(starts):
             succ[b].append(b + 1)
+    return starts, ends, succ
+
+
+def natural_loops(lines: list) -> list:
+    """The loops of a kernel's control flow: for every back edge (a branch to
+    a block that dominates it) the set of line indices of the loop's blocks.
+    Built from basic blocks, so a backward jump that only reflects block
+    placement is not a loop."""
+    starts, ends, succ = basic_blocks(lines)
     n = len(starts)
     pred = {b: [] for b in range(n)}
     for b, ss in succ.items():

@@ -263,17 +263,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
                 const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
                 m_run = m_new;
                 l_half *= alpha;
+                // a plain multiply: every operand of the loop fits in the
+                // 256 ordinary registers, so the products accumulate there
+                // and nothing moves between register files
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        // O *= alpha in place, in the accumulation register
-                        float e = oacc[db][r];
-                        float tmp;
-                        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                                     : "+a"(e), "=&v"(tmp) : "v"(alpha));
-                        oacc[db][r] = e;
-                    }
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             }
             // weights p = 2^(s c2 - m) (one FMA into the exponent), rounded to
             // the input type for the PV operands (keys 16ks .. 16ks+15 of the

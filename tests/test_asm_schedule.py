@@ -101,26 +101,43 @@ def test_every_barrier_kernel_is_recognised(kernels):
             assert expected_waits(n) is not None, n
 
 
+_SAVEEXEC = re.compile(r"s_and_saveexec_b64 (s\[\d+:\d+\])")
+_RESTORE = re.compile(r"s_or_b64 exec, exec, (s\[\d+:\d+\])")
+
+
 def check_no_barrier_under_saved_exec(kernels):
     for n, k in _barrier_kernels(kernels).items():
-        open_masks = []
-        for l in k["lines"]:
-            m = re.match(r"s_and_saveexec_b64 (s\[\d+:\d+\])", l)
-            if m:
-                open_masks.append(m.group(1))
-                continue
-            m = re.match(r"s_or_b64 exec, exec, (s\[\d+:\d+\])", l)
-            if m and m.group(1) in open_masks:
-                open_masks.remove(m.group(1))
-                continue
-            if l == "s_barrier":
-                assert not open_masks, f"{n}: s_barrier under saved exec {open_masks}"
+        lines = k["lines"]
+        starts, ends, succ = asm_info.basic_blocks(lines)
+        # masks still open on entry to each block, joined over every path
+        into = {0: frozenset()}
+        work = [0]
+        while work:
+            b = work.pop()
+            open_masks = set(into[b])
+            for l in lines[starts[b]:ends[b]]:
+                m = _SAVEEXEC.match(l)
+                if m:
+                    open_masks.add(m.group(1))
+                    continue
+                m = _RESTORE.match(l)
+                if m:
+                    open_masks.discard(m.group(1))
+                    continue
+                if l == "s_barrier":
+                    assert not open_masks, f"{n}: s_barrier under saved exec {sorted(open_masks)}"
+            for t in succ[b]:
+                joined = into.get(t, frozenset()) | open_masks
+                if t not in into or joined != into[t]:
+                    into[t] = frozenset(joined)
+                    work.append(t)
 
 
 def test_no_barrier_under_a_saved_exec_mask(kernels):
-    """Straight-line scan: s_and_saveexec opens a region only some lanes run,
-    the s_or_b64 exec that restores the saved mask closes it.  No barrier may
-    sit inside one."""
+    """s_and_saveexec opens a region only some lanes run, the s_or_b64 exec
+    that restores the saved mask closes it; the open masks follow the
+    control flow from block to block (a region that never closes runs to
+    the end of the program).  No barrier may be reachable inside one."""
     check_no_barrier_under_saved_exec(kernels)
 
 
