@@ -36,10 +36,15 @@
 //   is raised (and its O and sum scaled by 2^(m_old - m_new)) only when some
 //   row of the wave sees a logit more than 2^8 above its m; otherwise the
 //   block's weights are taken against the stale m (each at most 2^8).  O / l
-//   is the same either way.  The rescale multiplies O where the MFMAs keep
-//   it, in the accumulation registers (read, multiply, write back per
-//   value); written as a plain multiply, it makes the compiler keep a second
-//   copy of O in ordinary registers and refresh it on every key block.
+//   is the same either way.  Every operand of the loop (O, S, Q, the
+//   fragments and the row state) fits in a wave's 256 ordinary registers,
+//   where the MFMAs accumulate; nothing moves between register files.
+// * Wave priority (s_setprio) favours matrix products.  After each block's
+//   barrier the two waves of a SIMD start in step; raising the priority of
+//   the wave issuing MFMAs keeps the matrix core fed while the other runs
+//   its softmax.  At D = 128 each wave raises it for its two product phases;
+//   at D = 256 one wave of each pair (w < WAVES/2) keeps the higher priority
+//   throughout, which measured better there.
 // * The last key block, when Skv is not a multiple of BN, is peeled from the
 //   loop and masks keys >= Skv to -inf; K and V rows past Skv read as zero
 //   (the buffer range check).
@@ -110,6 +115,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;                             // half of the wave
+    constexpr bool kPhasePrio = D == 128;                // else priority by wave pair
+    if (!kPhasePrio && wave < WAVES / 2) __builtin_amdgcn_s_setprio(1);
     const float kNegInf = -__builtin_inff();
     const float kFar = POS ? kNegInf : __builtin_inff(); // a raw product no row max can pick
 
@@ -334,9 +341,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         for (; j < nfull; ++j) {
             publish();
             issue(j + STAGES - 1);
+            if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
             qk(j, s);
+            if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
             softmax.template operator()<false>(j, s, pf);
+            if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
             pv(j, pf);
+            if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
         }
         if constexpr (RAGGED) {
             publish();
