@@ -9,17 +9,21 @@ a call fails, an exception is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 __all__ = [
     "GemmError", "lib", "gemm_f16", "gemm_bf16", "gemm_batched_f16", "gemm_ex", "gemm_ex_bt", "gemm_ex_noalloc",
     "attention_fwd",
-    "variants", "select_variant", "LIB_PATH",
+    "variants", "select_variant", "library", "LIB_PATH", "POISON_LIB_PATH",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbpt_gemm.so")
+# the same library built with every LDS-DMA destination filled with NaN just
+# before its copy (race detection; build.build_poison)
+POISON_LIB_PATH = os.path.join(_PKG, "libbpt_gemm_poison.so")
 
 BPT_OK, BPT_ERR_INVALID_ARG, BPT_ERR_UNSUPPORTED, BPT_ERR_HIP = 0, 1, 2, 3
 
@@ -37,12 +41,29 @@ _lib = None
 def lib() -> ctypes.CDLL:
     """Load libbpt_gemm.so (built in-tree by __graft_entry__.build())."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"GEMM library not built: {LIB_PATH} is missing "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route this module's calls through another build of the library at
+    `path` (such as POISON_LIB_PATH) while the block runs; yields it."""
+    global _lib
+    saved = _lib
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"GEMM library not built: {path} is missing "
                            "(run __graft_entry__.build() or barrier_pipelined_tiled_amd/build.py)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     i64, p, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     L.gemm_f16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ci, p]
     L.gemm_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ci, p]
@@ -69,7 +90,6 @@ def lib() -> ctypes.CDLL:
     L.bpt_status_string.restype = ctypes.c_char_p
     L.bpt_last_error.argtypes = []
     L.bpt_last_error.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -5,6 +5,11 @@ kernel headers.  Packed-fp32 VALU forms are disabled for all device code.
 The same compilation keeps its gfx950 assembly (-save-temps, in ``_build/``)
 and writes ``libbpt_gemm.kernels.json`` beside the library: every kernel's
 resource use and a hash of its machine code (asm_info).
+
+``build_poison`` compiles the same source with ``BPT_LDS_POISON`` into
+``libbpt_gemm_poison.so``, a race-detection build whose every LDS-DMA copy
+first fills its destination with NaN (its assembly is kept in
+``_build/poison/``).
 """
 from __future__ import annotations
 
@@ -22,6 +27,9 @@ ARCH = "gfx950"
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 ASM_PATH = os.path.join(BUILD_DIR, f"api-hip-amdgcn-amd-amdhsa-{ARCH}.s")
 KERNELS_JSON = os.path.join(PKG_DIR, "libbpt_gemm.kernels.json")
+POISON_LIB_PATH = os.path.join(PKG_DIR, "libbpt_gemm_poison.so")
+POISON_BUILD_DIR = os.path.join(BUILD_DIR, "poison")
+POISON_ASM_PATH = os.path.join(POISON_BUILD_DIR, f"api-hip-amdgcn-amd-amdhsa-{ARCH}.s")
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
@@ -38,19 +46,25 @@ def hipcc() -> str:
     return path
 
 
-def build(out: str = LIB_PATH, extra: list[str] | None = None) -> str:
+def build(out: str = LIB_PATH, extra: list[str] | None = None, build_dir: str = BUILD_DIR) -> str:
     """Compile the library; returns the path of the shared object.  Also
-    keeps the device assembly and writes the kernel table (kernel_table)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    keeps the device assembly (in build_dir) and, for the library itself,
+    writes the kernel table (kernel_table)."""
+    os.makedirs(build_dir, exist_ok=True)
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-save-temps", *(extra or []), "-o", tmp, SRC]
-    res = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD_DIR)
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{res.stderr[-6000:]}")
     os.replace(tmp, out)
     if out == LIB_PATH:
         write_kernel_table()
     return out
+
+
+def build_poison() -> str:
+    """The LDS-poison race-detection build of the same source."""
+    return build(POISON_LIB_PATH, ["-DBPT_LDS_POISON"], POISON_BUILD_DIR)
 
 
 def write_kernel_table(asm_path: str = ASM_PATH, path: str = KERNELS_JSON) -> dict:
@@ -100,4 +114,5 @@ def device_asm(out_dir: str) -> str:
 
 if __name__ == "__main__":
     print(build())
+    print(build_poison())
     print(build_calib())

@@ -53,6 +53,21 @@ __device__ inline uint32_t lds_addr(const BPT_LDS void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
+#ifdef BPT_LDS_POISON
+// Race-detection build (libbpt_gemm_poison.so): right before a copy is
+// issued, its KiB of LDS is filled with 0x7fc0 halves, a NaN both as fp16 and
+// as bf16, and the write is waited for.  A read of a ring stage that is not
+// ordered after the copy's landing, or a copy issued while some wave still
+// reads the stage's previous contents, then turns into NaN in the result
+// instead of stale but plausible values.  The fill runs where the copy does,
+// after the same publish, so it adds no ordering of its own.
+__device__ inline void lds_poison_1k(uint32_t lds) {
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int4_t nan4 = {0x7fc07fc0, 0x7fc07fc0, 0x7fc07fc0, 0x7fc07fc0};
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(lds + 16u * lane), "v"(nan4) : "memory");
+}
+#endif
+
 // One wave-wide 16-byte-per-lane global->LDS copy (LDS-DMA).  Lane p's 16
 // bytes come from rsrc.base + voff + soff and land at lds + 16*p, i.e. one
 // contiguous KiB per wave.  The copy is counted by this wave's vmcnt and has
@@ -64,6 +79,9 @@ __device__ inline uint32_t lds_addr(const BPT_LDS void* p) {
 // serialises the pipeline.  Hidden from the compiler, these copies are
 // accounted for only by the explicit publish<>() waits below.
 __device__ inline void dma16(int4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+#ifdef BPT_LDS_POISON
+    lds_poison_1k(lds);
+#endif
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)

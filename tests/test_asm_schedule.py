@@ -15,7 +15,10 @@ compiler actually produced:
   count inside the K-loop, and the K-loop holds exactly one barrier per
   K-tile it runs per iteration;
 * no kernel spills ("Xe2 ESIMD GEMM", Workflow step 2): the GEMM kernels use
-  no scratch and spill no VGPR or SGPR.
+  no scratch and spill no VGPR or SGPR;
+* the race-detection build (libbpt_gemm_poison.so, run by
+  tests/test_lds_poison_gpu.py) fills every LDS-DMA copy's destination with
+  NaN, and waits for the fill, before issuing the copy.
 """
 import os
 import re
@@ -276,3 +279,44 @@ def test_attention_without_a_ragged_tail_spills_nothing(kernels):
             m = k["meta"]
             assert m["private_segment_fixed_size"] == 0 and m["vgpr_spill_count"] == 0, (n, m)
     assert seen == 16                          # {f16, bf16} x {16-bit, fp32 out} x {+,- scale} x {D 128, 256}
+
+
+def _is_copy(line):
+    return line.startswith("buffer_load_dwordx4") and line.endswith(" lds")
+
+
+@pytest.fixture(scope="module")
+def poison_kernels():
+    if not os.path.exists(build.POISON_ASM_PATH):
+        build.build_poison()
+    with open(build.POISON_ASM_PATH) as f:
+        return asm_info.kernels(f.read())
+
+
+def test_poison_build_fills_every_copy_destination_first(kernels, poison_kernels):
+    """Per kernel the poison build has the normal build's copies and exactly
+    one more ds_write_b128 per copy, and walking its code, no copy comes
+    without a ds_write_b128 and an lgkmcnt(0) wait since the previous copy
+    (the fill and the copy are adjacent statements, so no label separates
+    them)."""
+    assert set(poison_kernels) == set(kernels)
+    copies = 0
+    for n, k in poison_kernels.items():
+        lines, normal = k["lines"], kernels[n]["lines"]
+        nc = sum(map(_is_copy, lines))
+        assert nc == sum(map(_is_copy, normal)), n
+        writes = sum(l.startswith("ds_write_b128") for l in lines)
+        assert writes - sum(l.startswith("ds_write_b128") for l in normal) == nc, n
+        filled = waited = False
+        for l in lines:
+            if l.endswith(":"):
+                filled = waited = False
+            elif l.startswith("ds_write_b128"):
+                filled, waited = True, False
+            elif filled and l.startswith("s_waitcnt") and "lgkmcnt(0)" in l:
+                waited = True
+            elif _is_copy(l):
+                assert filled and waited, f"{n}: a copy without its fill"
+                filled = waited = False
+        copies += nc
+    assert copies > 0
