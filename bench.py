@@ -264,11 +264,13 @@ def clocks_under_load(torch, step, settle_s: float = 2.0, max_s: float = 20.0) -
     return r
 
 
-def time_steps(torch, step, args, stream):
+def time_steps(torch, step, args, stream, unit: int = 1):
     """The timing protocol: W untimed warm-up steps, the pause, the settle
     phase, then K timed steps between two synchronisations (wall clock and
     HIP events on the launch stream); then a per-call spread outside the
-    timed block.
+    timed block.  step(i) runs `unit` consecutive steps (a replayed graph of
+    one pass over the rotating sets with --graph, else one call); K must then
+    be a multiple of unit, and every figure is per step.
 
     The page's pause before timing is there so that the measurement starts
     at the GPU's steady frequency.  On MI355X a pause does the opposite: the
@@ -278,7 +280,10 @@ def time_steps(torch, step, args, stream):
     is followed by untimed steps for settle_ms of GPU time before the timed
     block.  The first K steps after the pause are timed too, on their own,
     and reported as after_pause -- they are not the value."""
-    for i in range(args.warmup):
+    if args.steps % unit:
+        raise SystemExit(f"--steps must be a multiple of {unit} (one graph replay runs {unit} steps)")
+    calls = args.steps // unit
+    for i in range(0, args.warmup, unit):
         step(i)
     torch.cuda.synchronize()
     if args.sleep > 0:
@@ -289,29 +294,29 @@ def time_steps(torch, step, args, stream):
         a0 = torch.cuda.Event(enable_timing=True)
         a1 = torch.cuda.Event(enable_timing=True)
         a0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(calls):
             step(i)
-            i += 1
+            i += unit
         a1.record(stream)
         torch.cuda.synchronize()
         after_ms = a0.elapsed_time(a1) / args.steps
-        n = max(0, int(args.settle_ms / after_ms) + 1 - args.steps)
+        n = max(0, (int(args.settle_ms / after_ms) + 1 - args.steps + unit - 1) // unit)
         for _ in range(n):
             step(i)
-            i += 1
+            i += unit
         torch.cuda.synchronize()
         settle = {"after_pause_ms_per_step": after_ms, "settle_ms": args.settle_ms,
-                  "settle_steps": args.steps + n}
+                  "settle_steps": args.steps + n * unit}
         log(f"after the pause: {after_ms:.4f} ms/step over the first {args.steps} steps; "
-            f"settled with {args.steps + n} untimed steps")
+            f"settled with {args.steps + n * unit} untimed steps")
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(calls):
         step(i)
-        i += 1
+        i += unit
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -320,18 +325,36 @@ def time_steps(torch, step, args, stream):
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (events)")
     # per-call spread, after and outside the timed block: each call between
     # its own pair of events on the launch stream
-    n_calls = min(50, max(10, args.steps // 4))
+    n_calls = min(50, max(10, calls // 4))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
     for a, b in evs:
         a.record(stream)
         step(i)
-        i += 1
+        i += unit
         b.record(stream)
     torch.cuda.synchronize()
-    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    per_call = sorted(a.elapsed_time(b) / unit for a, b in evs)
     pct = lambda q: per_call[min(len(per_call) - 1, int(q * len(per_call)))]
     spread = {"calls": n_calls, "p10_ms": pct(0.1), "median_ms": pct(0.5), "p90_ms": pct(0.9)}
+    if unit > 1:
+        spread["steps_per_call"] = unit
     return ms_per_step, kernel_ms, spread, settle
+
+
+def capture_pass(torch, step, steps: int, stream):
+    """One HIP graph holding `steps` consecutive steps (whole passes over the
+    rotating input sets, each step the same library call as without a
+    graph), captured on `stream` after one eager run of them; replay() runs
+    them again."""
+    for j in range(steps):
+        step(j)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for j in range(steps):
+            step(j)
+    torch.cuda.synchronize()
+    return g
 
 
 def roofline(flops, compulsory_bytes, kernel_ms):
@@ -370,7 +393,9 @@ def gemm_setup(torch, pkg, inputs, args, dev):
         out_t = torch.float32 if w.out_fp32 else (torch.float16 if w.dtype == "f16" else torch.bfloat16)
         Cs.append(torch.empty(w.c_shape(), dtype=out_t, device=dev))
     stream = torch.cuda.current_stream()
-    gemm = pkg.gemm_ex_bt if nt else pkg.gemm_ex
+    # under graph capture the split paths keep their splits only through the
+    # entry point that allocates nothing (its scratch is a fixed device array)
+    gemm = pkg.gemm_ex_bt if nt else (pkg.gemm_ex_noalloc if args.graph else pkg.gemm_ex)
 
     def step(i):
         j = i % R
@@ -467,6 +492,10 @@ def main():
     ap.add_argument("--b-layout", choices=["kn", "nt"], default="kn",
                     help="GEMM only.  kn: B is K x N (the workloads' layout); nt: the same B handed "
                          "over transposed (N x K) through gemm_ex_bt")
+    ap.add_argument("--graph", type=int, nargs="?", const=1, default=0, metavar="PASSES",
+                    help="capture PASSES passes over the rotating input sets (default 1) into one HIP "
+                         "graph and time its replays: each replay runs PASSES x rotating steps (for "
+                         "launch-bound shapes; --steps must be a multiple of that)")
     ap.add_argument("--record-traffic", metavar="RUN_DIR",
                     help="write profiles/traffic.json from the counter runs in RUN_DIR and exit")
     args = ap.parse_args()
@@ -486,6 +515,10 @@ def main():
 
     dev = torch.device("cuda:0")
     pkg.lib()
+    if args.graph:
+        # capture needs a stream other than the legacy default one; the whole
+        # run uses it (default priority)
+        torch.cuda.set_stream(torch.cuda.Stream())
     if args.workload in inputs.ATTENTION:
         setup = attention_setup
     elif args.workload in inputs.WORKLOADS:
@@ -498,8 +531,15 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident in HBM")
 
+    unit = 1
+    if args.graph:
+        unit = args.graph * w.rotating
+        graph = capture_pass(torch, step, unit, stream)
+        step = lambda i: graph.replay()
+        config["graph_steps_per_replay"] = unit
+        log(f"captured {args.graph} pass(es) over the {w.rotating} rotating sets ({unit} steps) into a graph")
     clk_before = None if args.no_clocks else smi_finish(smi_start())
-    ms_per_step, kernel_ms, spread, settle = time_steps(torch, step, args, stream)
+    ms_per_step, kernel_ms, spread, settle = time_steps(torch, step, args, stream, unit)
     clocks = None
     if not args.no_clocks:
         clocks = {"nominal_gfx_mhz": NOMINAL_GFX_MHZ, "before": clk_before,

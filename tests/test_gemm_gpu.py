@@ -394,6 +394,41 @@ def test_repack_full_size_odd_shape():
             assert np.array_equal(got.numpy(), ref)
 
 
+def test_graph_of_a_pass_over_rotating_sets():
+    """The launch-bound 256^3 shape as bench.py --graph runs it: one graph
+    holding the calls on several rotating (A, B, C) sets, captured on a
+    non-default stream.  Exact-integer inputs; every replay, with eager
+    calls and synchronisations between replays, gives each C the oracle's
+    RNE encoding bit for bit."""
+    M = N = K = 256
+    sets = []
+    for j in range(4):
+        A = inputs.small_integers((M, K), 7601 + 2 * j)
+        B = inputs.small_integers((K, N), 7602 + 2 * j)
+        ref = oracle.encode(oracle.gemm(inputs.bits(A), inputs.bits(B), "f16"), "f16")
+        sets.append((A.to(DEV), B.to(DEV), torch.empty((M, N), dtype=torch.float16, device=DEV), ref))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for A, B, C, _ in sets:                    # one eager pass first
+            pkg.gemm_f16(A, B, C, stream=s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for A, B, C, _ in sets:
+                pkg.gemm_f16(A, B, C, stream=s)
+        for rep in range(3):
+            for _, _, C, _ in sets:
+                C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for j, (A, B, C, ref) in enumerate(sets):
+                assert np.array_equal(as_bits(C.cpu()), ref), (rep, j)
+            eager = pkg.gemm_f16(sets[0][0], sets[0][1], stream=s)
+            torch.cuda.synchronize()
+            assert np.array_equal(as_bits(eager.cpu()), sets[0][3]), rep
+
+
 def test_graph_capture_of_a_repack_call():
     """Under graph capture the repack route may not use its workspace, so the
     guarded kernel takes the call; every replay must still be exact."""
