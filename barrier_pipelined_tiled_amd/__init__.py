@@ -116,19 +116,24 @@ def _stream_handle(stream):
 
 
 def _mat(t, name):
-    """(rows, cols, ld, batch_stride, batch) of a 2-D or 3-D row-major tensor."""
-    if t.dim() == 2:
-        t3 = t.unsqueeze(0)
-    elif t.dim() == 3:
-        t3 = t
+    """(rows, cols, ld, batch_stride, batch) of a 2-D or 3-D row-major tensor
+    (read from shape and strides directly: this runs three times per call)."""
+    shape = t.shape
+    st = t.stride()
+    if len(shape) == 2:
+        rows, cols = shape
+        srow, scol = st
+        batch, sb = 1, 0
+    elif len(shape) == 3:
+        batch, rows, cols = shape
+        sb, srow, scol = st
+        if batch <= 1:
+            sb = 0
     else:
-        raise ValueError(f"{name} must be 2-D or 3-D, got {tuple(t.shape)}")
-    batch, rows, cols = t3.shape
-    if cols > 1 and t3.stride(2) != 1:
+        raise ValueError(f"{name} must be 2-D or 3-D, got {tuple(shape)}")
+    if cols > 1 and scol != 1:
         raise ValueError(f"{name} must be contiguous in its last dimension")
-    ld = t3.stride(1) if rows > 1 else max(cols, 1)
-    sb = t3.stride(0) if batch > 1 else 0
-    return rows, cols, ld, sb, batch
+    return rows, cols, (srow if rows > 1 else max(cols, 1)), sb, batch
 
 
 _DT = {"f16": 0, "bf16": 1}
