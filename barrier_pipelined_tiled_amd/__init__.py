@@ -111,8 +111,15 @@ def _torch():
 
 def _stream_handle(stream):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    # the current stream's raw handle without building a Stream object (which
+    # costs about 3 us, as much as the library call); the public route when
+    # this torch build lacks the direct query
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(torch.cuda.current_device()))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _mat(t, name):
