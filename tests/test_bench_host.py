@@ -133,3 +133,70 @@ def test_smi_finish_reports_a_bad_reading_instead_of_raising():
     r = bench.smi_finish(proc)
     assert set(r) == {"error"}
     assert bench.smi_finish(None) is None
+
+
+class _Log:
+    """Stand-in for torch in time_steps: events and synchronisations append
+    markers to the same log as the steps, and every event pair times 1 ms."""
+
+    def __init__(self):
+        self.log = []
+        log = self.log
+
+        class Event:
+            def __init__(self, enable_timing=False):
+                pass
+
+            def record(self, stream=None):
+                log.append("event")
+
+            def elapsed_time(self, other):
+                return 1.0
+
+        class Cuda:
+            pass
+
+        self.cuda = Cuda()
+        self.cuda.Event = Event
+        self.cuda.synchronize = lambda: log.append("sync")
+
+
+@pytest.mark.parametrize("unit", [1, 8])
+def test_time_steps_times_exactly_k_steps(unit, monkeypatch):
+    """The timed block holds exactly K steps between two synchronisations
+    (K / unit calls when a call is a replayed graph of `unit` steps), after
+    at least W warm-up steps; every figure is per step."""
+    t = _Log()
+    calls = []
+
+    def step(i):
+        calls.append(i)
+        t.log.append(("step", i))
+
+    class Args:
+        steps, warmup, sleep, settle_ms = 64, 20, 0, 0
+    monkeypatch.setattr(bench, "log", lambda *a, **k: None)
+    ms, kernel_ms, spread, settle = bench.time_steps(t, step, Args, stream=None, unit=unit)
+    # the block: sync, event, K/unit calls, event, sync (the first event pair
+    # after the warm-up; settle_ms = 0 leaves no settle phase)
+    first_event = t.log.index("event")
+    assert t.log[first_event - 1] == "sync"
+    second_event = t.log.index("event", first_event + 1)
+    timed = [x for x in t.log[first_event:second_event] if isinstance(x, tuple)]
+    assert len(timed) == Args.steps // unit
+    assert t.log[second_event + 1] == "sync"
+    warm = [x for x in t.log[:first_event] if isinstance(x, tuple)]
+    assert len(warm) * unit >= Args.warmup
+    # step indices advance by unit, so replayed passes and plain calls see the
+    # same sequence of rotating sets
+    assert [i for _, i in timed] == list(range(timed[0][1], timed[0][1] + Args.steps, unit))
+    assert kernel_ms == pytest.approx(1.0 / Args.steps)
+    assert spread["median_ms"] == pytest.approx(1.0 / unit)
+    assert settle is None
+
+
+def test_time_steps_refuses_a_step_count_that_splits_a_replay():
+    class Args:
+        steps, warmup, sleep, settle_ms = 100, 20, 0, 0
+    with pytest.raises(SystemExit):
+        bench.time_steps(_Log(), lambda i: None, Args, stream=None, unit=8)
