@@ -40,6 +40,21 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, name), f"{name} declared in bpt_gemm.h but not exported"
 
 
+def test_the_poison_build_exports_the_same_boundary():
+    """The race-detection build (every LDS-DMA destination NaN-filled before
+    its copy) is the same library: it loads without a GPU, exports every
+    declared function and has the same variant table."""
+    if not os.path.exists(pkg.POISON_LIB_PATH):
+        from barrier_pipelined_tiled_amd import build
+        build.build_poison()
+    normal = pkg.variants()
+    with pkg.library(pkg.POISON_LIB_PATH) as P:
+        for name in declared_functions():
+            assert hasattr(P, name), f"{name} not exported by the poison build"
+        assert pkg.variants() == normal
+    assert pkg.lib() is not P
+
+
 def test_no_torch_types_in_header():
     text = open(HEADER).read()
     assert "at::Tensor" not in text and "c10" not in text
