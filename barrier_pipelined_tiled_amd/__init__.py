@@ -49,7 +49,9 @@ def lib() -> ctypes.CDLL:
 @contextlib.contextmanager
 def library(path: str):
     """Route this module's calls through another build of the library at
-    `path` (such as POISON_LIB_PATH) while the block runs; yields it."""
+    `path` (such as POISON_LIB_PATH) while the block runs; yields it.  The
+    switch is process-wide: calls from other threads during the block use
+    that build too."""
     global _lib
     saved = _lib
     _lib = _load(path)
