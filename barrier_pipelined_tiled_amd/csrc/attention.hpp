@@ -19,8 +19,9 @@
 //   at head dimension 256 that holds for 32-key blocks.
 // * K and V blocks of BN keys are staged global->LDS by LDS-DMA in a ring of
 //   STAGES stages.  Block j is published by a vmcnt wait plus one s_barrier;
-//   right after it the copies of block j+STAGES-1 are issued into the stage
-//   block j-1 left (the window), and the math of block j follows.
+//   the copies of block j+STAGES-1 into the stage block j-1 left (the
+//   window) go out between block j's first products, and the rest of its
+//   math follows.
 // * The K and V fragments for the matrix products are read from LDS two
 //   MFMAs ahead of their use.  With both fragment reads and the O and Q
 //   registers a wave holds, the compiler otherwise kept one fragment in
@@ -174,13 +175,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         }
         const uint32_t ldsb = __builtin_amdgcn_readfirstlane(lds_addr(lds));
         const uint32_t kstepK = (uint32_t)(BN * a.ldk * 2), kstepV = (uint32_t)(BN * a.ldv * 2);
-        // block j into stage j % STAGES (blocks past the last read zeros)
-        auto issue = [&](int j) __attribute__((always_inline)) {
+        // block j into stage j % STAGES (blocks past the last read zeros):
+        // copy c < COPIES is a KiB of K, the others of V
+        auto copy = [&](int j, int c) __attribute__((always_inline)) {
             const uint32_t st = ldsb + (j & (STAGES - 1)) * G::STAGE + wave * G::COPIES * 1024;
+            if (c < G::COPIES)
+                dma16(rsK, st + c * 1024, voffK[c] + j * kstepK, 0);
+            else
+                dma16(rsV, st + G::TILE + (c - G::COPIES) * 1024, voffV[c - G::COPIES] + j * kstepV, 0);
+        };
+        auto issue = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < G::COPIES; ++i) dma16(rsK, st + i * 1024, voffK[i] + j * kstepK, 0);
-#pragma unroll
-            for (int i = 0; i < G::COPIES; ++i) dma16(rsV, st + G::TILE + i * 1024, voffV[i] + j * kstepV, 0);
+            for (int c = 0; c < 2 * G::COPIES; ++c) copy(j, c);
         };
 
         // fragment reads.  K (row operand of S^T = K Q^T): key 32kb + l%32,
@@ -208,7 +214,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         // scheduling fences keep that order (without the one before the
         // MFMA, the compiler moved the read below it).
         constexpr int PD = 2;
-        auto qk = [&](int j, float16_t (&s)[G::KB]) __attribute__((always_inline)) {
+        // With COPY, the copies of block cj go out between the products, one
+        // after every SPREAD-th MFMA: issued together after the barrier, the
+        // eight waves' copies queued behind each other for the address unit
+        // and held each wave 150-350 cycles before its first product.
+        auto qk = [&]<bool COPY>(int j, int cj, float16_t (&s)[G::KB]) __attribute__((always_inline)) {
             const uint32_t kj = kbase + (uint32_t)((j & (STAGES - 1)) * G::STAGE);
             constexpr int N = TS * G::KB;
             auto kread = [&](int i) __attribute__((always_inline)) {
@@ -228,6 +238,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
                 const int t = i / G::KB, kb = i % G::KB;
                 s[kb] = Mfma<T>::mma32(kf[i % (PD + 1)], qf[t], s[kb]);
                 __builtin_amdgcn_sched_barrier(0);
+                constexpr int SPREAD = N / (2 * G::COPIES);
+                static_assert(SPREAD >= 1 && N % (2 * G::COPIES) == 0, "copies spread evenly over the products");
+                if constexpr (COPY)
+                    if (i % SPREAD == 1 % SPREAD) copy(cj, i / SPREAD);
             }
         };
         // the online softmax of block j: running max, rescale of O and the
@@ -321,8 +335,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         };
 
         // Ring of STAGES: blocks 0 .. STAGES-2 are copied ahead; step j
-        // publishes block j, then copies block j+STAGES-1 into the stage
-        // block j-1 left.  Copies are issued past the last block too (they
+        // publishes block j, then, during its S products, copies block
+        // j+STAGES-1 into the stage block j-1 left.  Copies are issued past
+        // the last block too (they
         // read zeros), so every publish lets the same STAGES-2 younger
         // blocks stay in flight.
         // publish block j: this wave's copies of it landed (vmcnt), every
@@ -340,9 +355,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         int j = 0;
         for (; j < nfull; ++j) {
             publish();
-            issue(j + STAGES - 1);
             if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
-            qk(j, s);
+            qk.template operator()<true>(j, j + STAGES - 1, s);
             if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
             softmax.template operator()<false>(j, s, pf);
             if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(1);
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attention_fwd_kernel(AttnArgs a
         }
         if constexpr (RAGGED) {
             publish();
-            qk(j, s);
+            qk.template operator()<false>(j, 0, s);
             softmax.template operator()<true>(j, s, pf);
             pv(j, pf);
         }
