@@ -20,6 +20,7 @@
 #include "gemm_apair.hpp"
 #include "gemm_persist.hpp"
 #include "gemm_persist_ares.hpp"
+#include "gemm_persist_roles.hpp"
 #include "gemm_generic.hpp"
 #include "gemm_pipelined.hpp"
 #include "gemm_skinny.hpp"
@@ -64,7 +65,8 @@ enum Variant {
     V_SPLITK = 18,          // few output tiles: K split over the pipelined kernel's batch, + split-sum kernel
     V_PERSIST_AP = 19,      // the persistent short-K kernel with A copied in K-tile pairs (whole lines)
     V_PERSIST_AR = 20,      // the persistent short-K kernel walking row blocks with their A panel kept in LDS
-    V_COUNT = 20
+    V_PERSIST_RL = 21,      // the A-resident short-K kernel with wave roles: compute, copy and store waves
+    V_COUNT = 21
 };
 
 bool is_bt_variant(int v) { return (v >= V_BT_256_K32_S4 && v <= V_BT_256_K64_S2) || v == V_BT_256_K32_S4_AP; }
@@ -91,11 +93,12 @@ const char* const kVariantNames[] = {
     "splitk_pipelined",
     "persistent_256x128x32_shortk_apair",
     "persistent_256x128x32_shortk_aresident",
+    "persistent_128x256x32_shortk_roles",
 };
 
 // K-tile and stage count of each pipelined variant (0 for the others)
-constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0, 32, 32};
-constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0, 4, 3};
+constexpr int kVariantBK[] = {0, 0, 64, 64, 32, 32, 32, 0, 0, 0, 32, 32, 0, 64, 32, 0, 32, 32, 0, 32, 32, 32};
+constexpr int kVariantStages[] = {0, 0, 2, 2, 4, 5, 4, 0, 0, 0, 4, 4, 0, 2, 4, 0, 4, 4, 0, 4, 3, 4};
 // which of them take K % BK != 0 (see pipelined_ok); filled below from the
 // kernels' own layout
 bool variant_tail(int v);
@@ -469,6 +472,16 @@ bool persist_ok(const Call& c) {
     return total >= 256 && total <= kI31;
 }
 
+// the persistent kernel with wave roles: whole 128 x 256 tiles, K = 128 or
+// 256, 16-bit C, and at least one row block per CU
+bool persist_roles_ok(const Call& c) {
+    if (c.bt || c.out_fp32 || (c.K != 128 && c.K != 256) || c.M % 128 != 0 || c.N % 256 != 0) return false;
+    if (!pipelined_ok(c, 32, 4, false)) return false;
+    if (!aligned16(c.C) || (c.ldc * 2) % 16 != 0 || (c.sC * 2) % 16 != 0) return false;
+    const long long groups = (c.M / 128) * c.batch;
+    return groups >= 256 && groups * (c.N / 256) <= kI31;
+}
+
 int choose_pipelined(const Call& c) {
     const long long tiles256 = ((c.M + 255) / 256) * ((c.N + 255) / 256) * c.batch;
     const bool big = tiles256 >= 128;
@@ -481,6 +494,12 @@ int choose_pipelined(const Call& c) {
     // With K = 128 the kernel that keeps each row block's A panel in LDS and
     // streams only B: 64 x 4096^2 x 128 0.493 -> 0.466 ms; with K = 256 its
     // 3-stage ring leaves the stores no room and it is slower (0.90 ms)
+    // Wave roles (compute, copy and store waves, the A panel in LDS): the
+    // copies' waits no longer count stores; on one machine, alternating,
+    // 64 x 4096^2 x 256 0.690 -> 0.611 ms against the A-pair kernel,
+    // K = 128 0.455 -> 0.396 ms against the A-resident one, and 7-30% on
+    // six other batched shapes of 4096 to 8192 tiles
+    if (persist_roles_ok(c) && (c.M / 128) * (c.N / 256) * c.batch >= 2048) return V_PERSIST_RL;
     if (persist_ok(c) && (c.M / 256) * (c.N / 128) * c.batch >= 2048) return c.K == 128 ? V_PERSIST_AR : V_PERSIST_AP;
     // whole-line A copies: 4096^3 1230 -> 1270 TFLOP/s, 4096 x 4096 x 16384
     // 1393 -> 1417 against the 32-wide 4-stage kernel on the same machine
@@ -754,6 +773,31 @@ hipError_t launch_persist_ares(const Call& c, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Groups are whole row blocks (128 rows, all N / 256 column tiles); one
+// workgroup of 8 waves per CU.
+template <typename T, typename OutT>
+hipError_t launch_persist_roles(const Call& c, hipStream_t stream) {
+    bpt::GemmArgs a;
+    a.A = c.A; a.B = c.B; a.C = c.C;
+    a.M = (int)c.M; a.N = (int)c.N; a.K = (int)c.K;
+    a.lda = (int)c.lda; a.ldb = (int)c.ldb; a.ldc = (int)c.ldc;
+    a.strideA = c.sA; a.strideB = c.sB; a.strideC = c.sC;
+    a.tiles_m = (int)(c.M / 128);
+    a.tiles_n = (int)(c.N / 256);
+    a.group_m = 1;
+    a.c_vec = 1;
+    a.nb = (int)c.N;
+    const int ngroups = (int)((long long)a.tiles_m * c.batch);
+    const int grid = 256;                                  // persist_roles_ok: ngroups >= 256
+    if (c.K == 256)
+        hipLaunchKernelGGL((bpt::gemm_persist_roles_kernel<T, OutT, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+                           ngroups, a.tiles_n);
+    else
+        hipLaunchKernelGGL((bpt::gemm_persist_roles_kernel<T, OutT, 4>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+                           ngroups, a.tiles_n);
+    return hipGetLastError();
+}
+
 template <typename T, typename OutT>
 hipError_t launch_skinny(const Call& c, hipStream_t stream) {
     bpt::SkinnyArgs a;
@@ -953,6 +997,9 @@ hipError_t dispatch_typed(const Call& c, int v, hipStream_t stream) {
         case V_PERSIST_AR:
             if constexpr (sizeof(OutT) == 2) return launch_persist_ares<T, OutT>(c, stream);
             return hipErrorInvalidValue;
+        case V_PERSIST_RL:
+            if constexpr (sizeof(OutT) == 2) return launch_persist_roles<T, OutT>(c, stream);
+            return hipErrorInvalidValue;
         default: return launch_generic<T, OutT>(c, stream);
     }
 }
@@ -1000,6 +1047,7 @@ bool variant_accepts(const Call& c, int v) {
         case V_PERSIST:
         case V_PERSIST_AP:
         case V_PERSIST_AR: return persist_ok(c);
+        case V_PERSIST_RL: return persist_roles_ok(c);
         default:
             if (v > V_GENERIC && v < V_SKINNY) return pipelined_ok(c, kVariantBK[v], kVariantStages[v], variant_tail(v));
             return false;

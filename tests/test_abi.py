@@ -150,12 +150,19 @@ def test_automatic_variant_choice():
     apair = v["pipelined_256x256x32_s4_apair"]
     assert pkg.select_variant("f16", 1, 4096, 4096, 4096, 4096, 4096) == apair
     assert pkg.select_variant("bf16", 1, 4096, 4096, 16384, 16384, 4096, True) == apair
-    # short K over >= 2048 tiles of 256 x 128 (16-bit C): the persistent kernel
+    # short K over >= 256 row blocks of 128 and >= 2048 tiles of 128 x 256
+    # (16-bit C): the persistent kernel with wave roles, K = 256 and 128
+    roles = v["persistent_128x256x32_shortk_roles"]
+    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == roles
+    assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == roles
+    assert pkg.select_variant("f16", 8, 4096, 4096, 256, 256, 4096) == roles
+    # fewer row blocks, >= 2048 tiles of 256 x 128: the A-pair persistent kernel,
+    # at K = 128 the one keeping each row block's A panel in LDS
     persist = v["persistent_256x128x32_shortk_apair"]
-    assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096) == persist
-    # K = 128: the kernel keeping each row block's A panel in LDS
-    assert pkg.select_variant("bf16", 64, 4096, 4096, 128, 128, 4096) == v["persistent_256x128x32_shortk_aresident"]
     assert pkg.select_variant("f16", 4, 4096, 4096, 256, 256, 4096) == persist
+    assert pkg.select_variant("f16", 4, 4096, 4096, 128, 128, 4096) == v["persistent_256x128x32_shortk_aresident"]
+    # N not a multiple of 256: the A-pair persistent kernel
+    assert pkg.select_variant("f16", 64, 4096, 4224, 256, 256, 4224) == persist
     assert pkg.select_variant("f16", 2, 4096, 4096, 256, 256, 4096) == apair      # 1024 tiles
     assert pkg.select_variant("f16", 64, 4096, 4096, 256, 256, 4096, True) == apair   # fp32 C
     assert pkg.select_variant("f16", 64, 4096, 4096, 192, 192, 4096) == apair     # K not 128 or 256

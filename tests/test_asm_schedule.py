@@ -100,8 +100,8 @@ def test_every_barrier_kernel_is_recognised(kernels):
     names = _barrier_kernels(kernels)
     assert names
     for n in names:
-        if asm_info.base_name(n) not in ("gemm_generic_kernel", "gemm_skinny_kernel"):
-            assert expected_waits(n) is not None, n
+        if asm_info.base_name(n) not in ("gemm_generic_kernel", "gemm_skinny_kernel", "gemm_persist_roles_kernel"):
+            assert expected_waits(n) is not None, n           # the roles kernel: its own test below
 
 
 _SAVEEXEC = re.compile(r"s_and_saveexec_b64 (s\[\d+:\d+\])")
@@ -186,6 +186,46 @@ def test_publish_waits_match_the_ring(kernels):
     check_publish_waits(kernels)
 
 
+def check_roles_barriers(kernels):
+    """The persistent kernel with wave roles: only its copy waves issue
+    copies, so only their publish waits on vmcnt, for the ring's two younger
+    windows (2 x 8 copies), and on a new A panel for the window issued after
+    it (8); the compute and store waves publish with lgkmcnt(0) alone; the
+    extra barrier of a new row block sits behind a uniform branch.  The
+    compute loop (one tile, unrolled) holds one publish per K-tile plus that
+    barrier, the copy and store loops one publish plus it; no loop with a
+    barrier writes exec."""
+    seen = 0
+    for n, k in kernels.items():
+        if asm_info.base_name(n) != "gemm_persist_roles_kernel":
+            continue
+        seen += 1
+        (nk,) = _ints(n)
+        L = k["lines"]
+        bars = [i for i, l in enumerate(L) if l == "s_barrier"]
+        allowed = {"s_waitcnt vmcnt(16) lgkmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_waitcnt vmcnt(8)"}
+        kinds = {}
+        for i in bars:
+            prev = L[i - 1]
+            if prev.startswith("s_cbranch_"):
+                prev = "branch"
+            assert prev in allowed | {"branch"}, (n, prev)
+            kinds[prev] = kinds.get(prev, 0) + 1
+        assert kinds.get("s_waitcnt vmcnt(16) lgkmcnt(0)", 0) >= 1 and kinds.get("s_waitcnt vmcnt(8)", 0) == 1, kinds
+        per_loop = sorted(sum(1 for i in lp if L[i] == "s_barrier") for lp in _loops(L)
+                          if any(L[i] == "s_barrier" for i in lp))
+        assert per_loop == [2, 2, nk + 1], (n, per_loop)
+        for lp in _loops(L):
+            if any(L[i] == "s_barrier" for i in lp):
+                writes = [L[i] for i in sorted(lp) if _EXEC_WRITE.match(L[i])]
+                assert not writes, (n, writes[:3])
+    assert seen == 4                           # {f16, bf16} x {K = 128, 256}
+
+
+def test_roles_kernel_barriers(kernels):
+    check_roles_barriers(kernels)
+
+
 APAIR = "_ZN3bpt17gemm_apair_kernelIDF16_DF16_Lb0EEEvNS_8GemmArgsE"
 
 
@@ -234,7 +274,7 @@ def test_the_checks_catch_planted_mistakes(kernels):
 
 
 GEMM_TEMPLATES = ("gemm_pipelined_kernel", "gemm_apair_kernel", "gemm_persist_kernel", "gemm_persist_apair_kernel",
-                  "gemm_persist_ares_kernel", "gemm_skinny_kernel",
+                  "gemm_persist_ares_kernel", "gemm_persist_roles_kernel", "gemm_skinny_kernel",
                   "gemm_skinny_ring_kernel", "gemm_generic_kernel", "skinny_sum_kernel", "splitk_sum_kernel",
                   "repack_pad_kernel", "fill_zero_kernel")
 

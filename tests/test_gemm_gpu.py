@@ -290,6 +290,79 @@ def test_persistent_repeated_calls(vname):
         assert torch.equal(o, outs[0])
 
 
+# the persistent kernel with wave roles: whole 128 x 256 tiles, K = 128 or
+# 256, 16-bit C, at least 256 row blocks.  256 row blocks (one per
+# workgroup), 320 (some workgroups walk two, reloading the A panel mid-walk),
+# 3 column tiles per row, and 1 (a new panel every tile).
+ROLES = "persistent_128x256x32_shortk_roles"
+ROLES_SHAPES = [("f16", 8, 4096, 1024, 256), ("f16", 10, 4096, 512, 256), ("bf16", 16, 2048, 768, 256),
+                ("f16", 9, 4096, 256, 128), ("bf16", 64, 512, 512, 128)]
+
+
+@pytest.mark.parametrize("dtype,batch,M,N,K", ROLES_SHAPES)
+def test_roles_parity(dtype, batch, M, N, K):
+    v = pkg.variants()[ROLES]
+    say(f"[roles] {dtype} batch={batch} M={M} N={N} K={K}")
+    A = inputs.uniform((batch, M, K), 7801 + M + N, dtype=dtype, nonzero=True)
+    B = inputs.uniform((batch, K, N), 7802 + M + N, dtype=dtype, nonzero=True)
+    check_random(A, B, dtype, False, v)
+    Ai = inputs.small_integers((batch, M, K), 7803, dtype=dtype)
+    Bi = inputs.small_integers((batch, K, N), 7804, dtype=dtype)
+    got = run(Ai, Bi, dtype, False, v)
+    assert np.array_equal(as_bits(got), oracle.encode(oracle.gemm(inputs.bits(Ai), inputs.bits(Bi), dtype), dtype))
+
+
+@pytest.mark.parametrize("K", [256, 128])
+def test_roles_match_the_pair_kernel_bitwise(K):
+    """The wave-role kernel and the A-pair persistent kernel run the same
+    products in the same order: bitwise equal C on random inputs."""
+    V = pkg.variants()
+    b, M, N = 12, 4096, 1024                      # 384 row blocks: uneven walks
+    say(f"[roles vs pair] b={b} M={M} N={N} K={K}")
+    A = inputs.uniform((b, M, K), 7811 + K, nonzero=True).to(DEV)
+    B = inputs.uniform((b, K, N), 7812 + K, nonzero=True).to(DEV)
+    r = pkg.gemm_ex(A, B, variant=V[ROLES])
+    q = pkg.gemm_ex(A, B, variant=V["persistent_256x128x32_shortk_apair"])
+    torch.cuda.synchronize()
+    assert torch.equal(r.view(torch.int16), q.view(torch.int16))
+
+
+@pytest.mark.parametrize("K", [256, 128])
+def test_roles_padded_views_nan_padding(K):
+    """lda > K, ldb > N, ldc > N and batch strides from padded tensors, NaN in
+    every padding element of A and B: correct, and C's padding untouched."""
+    v = pkg.variants()[ROLES]
+    b, M, N = 8, 4096, 512
+    say(f"[roles padded] b={b} M={M} N={N} K={K}")
+    A = inputs.uniform((b, M, K), 7821 + K, nonzero=True)
+    B = inputs.uniform((b, K, N), 7822 + K, nonzero=True)
+    Ap = torch.full((b, M, K + 8), float("nan"), dtype=torch.float16)
+    Ap[:, :, :K] = A
+    Bp = torch.full((b, K, N + 24), float("nan"), dtype=torch.float16)
+    Bp[:, :, :N] = B
+    Cp = torch.full((b, M, N + 8), 7.0, dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(Ap.to(DEV)[:, :, :K], Bp.to(DEV)[:, :, :N], Cp[:, :, :N], variant=v)
+    torch.cuda.synchronize()
+    Cp = Cp.cpu()
+    assert torch.all(Cp[:, :, N:] == 7.0)
+    m = oracle.compare(Cp[:, :, :N].float().numpy(), oracle.gemm(inputs.bits(A), inputs.bits(B)), K)
+    assert m["ok"], m
+
+
+def test_roles_repeated_calls():
+    """Back-to-back calls on one stream, the last into a NaN-filled C: every
+    call writes every tile once, bit-identical each time."""
+    v = pkg.variants()[ROLES]
+    A = inputs.uniform((10, 4096, 256), 7831, nonzero=True).to(DEV)
+    B = inputs.uniform((10, 256, 512), 7832, nonzero=True).to(DEV)
+    outs = [pkg.gemm_ex(A, B, variant=v) for _ in range(4)]
+    C = torch.full((10, 4096, 512), float("nan"), dtype=torch.float16, device=DEV)
+    pkg.gemm_ex(A, B, C, variant=v)
+    torch.cuda.synchronize()
+    for o in outs[1:] + [C]:
+        assert torch.equal(o, outs[0])
+
+
 def test_batched_entry_point():
     b, M, N, K = 4, 256, 256, 256
     A = inputs.uniform((b, M, K), 7101, lo=-0.5, hi=0.5)
@@ -955,7 +1028,7 @@ def test_operand_over_2gib_runs_on_64bit_offsets():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("out_fp32,vname", [(False, "persistent_256x128x32_shortk_apair"),
+@pytest.mark.parametrize("out_fp32,vname", [(False, "persistent_128x256x32_shortk_roles"),
                                             (True, "pipelined_256x256x32_s4_apair")])
 def test_single_output_over_2gib(out_fp32, vname):
     """One C of 32768 x 32768 (2 GiB in fp16, 4 GiB in fp32) from the fast

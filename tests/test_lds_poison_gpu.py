@@ -109,6 +109,19 @@ def test_persistent_kernels_poison(vname, batch, M, N, K):
     same_and_finite(ref, got)
 
 
+# the wave-role kernel: copy waves fill the B ring and the A panel, store
+# waves read the C slots; 320 row blocks (panels reloaded mid-walk), and one
+# column tile per row block (a new panel every tile)
+@pytest.mark.parametrize("batch,M,N,K", [(10, 4096, 512, 256), (9, 4096, 256, 128), (10, 4096, 512, 128)])
+def test_roles_kernel_poison(batch, M, N, K):
+    say(f"[poison] roles {batch}x{M}x{N}x{K}")
+    A = inputs.uniform((batch, M, K), 9351 + K, nonzero=True).to(DEV)
+    B = inputs.uniform((batch, K, N), 9352 + K, nonzero=True).to(DEV)
+    v = pkg.variants()["persistent_128x256x32_shortk_roles"]
+    ref, got = both(lambda: pkg.gemm_ex(A, B, variant=v))
+    same_and_finite(ref, got)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("BH,Sq,Skv,D", [(2, 300, 257, 256), (2, 512, 4096, 256), (3, 256, 96, 128),
                                          (2, 512, 4000, 128), (1, 100, 31, 256)])
