@@ -13,7 +13,9 @@ compiler actually produced:
   s_waitcnt vmcnt(n) lgkmcnt(0), with n one of the wait counts the kernel's
   ring implies (closed forms of its template parameters below), the steady
   count inside the K-loop, and the K-loop holds exactly one barrier per
-  K-tile it runs per iteration;
+  K-tile it runs per iteration; in the persistent kernel with wave roles
+  only the copy waves wait on vmcnt, and the other roles publish with
+  lgkmcnt(0) alone (its own check);
 * no kernel spills ("Xe2 ESIMD GEMM", Workflow step 2): the GEMM kernels use
   no scratch and spill no VGPR or SGPR;
 * the race-detection build (libbpt_gemm_poison.so, run by
