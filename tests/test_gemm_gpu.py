@@ -306,9 +306,12 @@ def test_roles_parity(dtype, batch, M, N, K):
     A = inputs.uniform((batch, M, K), 7801 + M + N, dtype=dtype, nonzero=True)
     B = inputs.uniform((batch, K, N), 7802 + M + N, dtype=dtype, nonzero=True)
     check_random(A, B, dtype, False, v)
+    # into a NaN-filled C: each workgroup walks its row blocks' column tiles
+    # in a rotated order, and every tile must be written exactly once
     Ai = inputs.small_integers((batch, M, K), 7803, dtype=dtype)
     Bi = inputs.small_integers((batch, K, N), 7804, dtype=dtype)
-    got = run(Ai, Bi, dtype, False, v)
+    C = torch.full((batch, M, N), float("nan"), dtype=torch.float16 if dtype == "f16" else torch.bfloat16, device=DEV)
+    got = run(Ai, Bi, dtype, False, v, C=C)
     assert np.array_equal(as_bits(got), oracle.encode(oracle.gemm(inputs.bits(Ai), inputs.bits(Bi), dtype), dtype))
 
 
