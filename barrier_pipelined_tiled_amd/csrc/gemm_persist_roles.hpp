@@ -33,13 +33,14 @@
 // g-1, and store its rows as whole 128-byte lines.  A slot is rewritten two
 // steps after it was filled, after the store waves' reads of it retired.
 //
-// A new row block: after publish(g) of its first K-tile every wave is done
-// with the old panel; the copy waves copy the new one, wait for it and every
-// wave meets at one more s_barrier before the products go on.
+// A new row block: its A panel replaces the old one a pair stage (64 k) at
+// a time while the old row block's last tile runs, each pair as soon as that
+// tile has read it for the last time; the ordinary publish waits cover the
+// new pairs (see the copy loop), so no wave waits for a whole panel.
 //
 // The last tile's C goes out in NK more steps without products, and one
 // more step stores the last slot, so every wave executes the same
-// (turns + 1) * NK + 1 publishes plus one barrier per new row block.
+// (turns + 1) * NK + 1 publishes.
 //
 // LDS (K = 256): panel 64 KiB (4 pair stages of 128 rows x 64 k, as the
 // A-pair kernel lays them out), B ring 64 KiB, two C slots of 8 KiB; 144 KiB.
@@ -79,7 +80,6 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
     constexpr int STG_BASE = B_BASE + BSTAGES * B_BYTES;
     constexpr int LDS_BYTES = STG_BASE + 2 * SLOT;
     constexpr int WIN = B_BYTES / 1024 / 2;              // copies per copy wave per K-tile
-    constexpr int PANEL_INST = PANEL / 1024 / 2;         // panel copies per copy wave
     constexpr int PAIR_INST = AP_BYTES / 1024;           // copies per pair stage
     constexpr int VM = (BSTAGES - 2) * WIN;              // younger copies at a publish
     constexpr int RD = WSLOT / 1024;                     // 1 KiB reads per wave part of a slot
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
     static_assert(sizeof(OutT) == 2, "16-bit C: slots of 128-byte rows");
     static_assert(RPK == 16 || RPK == 32, "half or whole 32-row blocks per step");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-    static_assert(VM + WIN < 64 && PANEL_INST + 3 * WIN < 64, "vmcnt");
+    static_assert(VM + WIN < 64 && 2 * PAIR_INST + 3 * WIN < 64, "vmcnt");
     typedef typename Mfma<T>::frag_t frag_t;
     __shared__ __attribute__((aligned(1024))) char lds_raw[LDS_BYTES];
     BPT_LDS char* lds = (BPT_LDS char*)lds_raw;
@@ -102,15 +102,9 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
     const int ksteps_total = t_mma + NK;   // + the steps that send the last tile
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
-    // a new row block starts at step g (g > 0)
-    auto new_group = [&](int g) __attribute__((always_inline)) {
-        if (g == 0 || g >= t_mma || g % NK != 0) return false;
-        return (g / NK) % gn == 0;
-    };
     auto publish_lgkm = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    auto barrier = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
     // batch entry and corner of tile number `it` of this workgroup (the
     // divisions run on VGPR copies, as in the other persistent kernels)
     auto corner = [&](int it, int& batch, int& m0, int& n0) __attribute__((always_inline)) {
@@ -173,9 +167,9 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
 #pragma unroll
             for (int i = 0; i < WIN; ++i) dma16(rs, st + i * 1024, voffB[i], (uint32_t)k * b_step);
         };
-        // the A panel of tile it's row block: pair stage p holds k 64p ..
-        // 64p+63 of 128 rows, 8 rows of 128 bytes per copy
-        auto panel = [&](int it) __attribute__((always_inline)) {
+        // pair stage p of tile it's A panel: k 64p .. 64p+63 of the row
+        // block's 128 rows, 8 rows of 128 bytes per copy, this wave's half
+        auto pair = [&](int it, int p) __attribute__((always_inline)) {
             int batch, m0, n0;
             corner(it, batch, m0, n0);
             const T* a0 = static_cast<const T*>(args.A) + batch * args.strideA + (long long)m0 * lda;
@@ -183,30 +177,32 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
 #pragma unroll
             for (int q = 0; q < 4; ++q) ra[q] = __builtin_amdgcn_readfirstlane(ra[q]);
 #pragma unroll
-            for (int i = 0; i < PANEL_INST; ++i) {
-                const int c = cw * PANEL_INST + i;
-                const int p = c / PAIR_INST, ii = c % PAIR_INST;
+            for (int i = 0; i < PAIR_INST / 2; ++i) {
+                const int ii = cw * (PAIR_INST / 2) + i;
                 const int row = ii * 8 + lane / 8;
                 const int chunk = (lane % 8) ^ swz_a<64>(row);
                 dma16(ra, lds0 + p * AP_BYTES + ii * 1024, (uint32_t)((row * lda + chunk * 8) * 2),
                       (uint32_t)(p * 2 * BK * 2));
             }
         };
-        panel(0);
+#pragma unroll
+        for (int p = 0; p < NK / 2; ++p) pair(0, p);
 #pragma unroll
         for (int g = 0; g < BSTAGES - 1; ++g) window(g);
         for (int g = 0; g <= ksteps_total; ++g) {
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
-            if (new_group(g)) {
-                // every wave is done with the old panel: copy the new one,
-                // then K-tile g+3, and wait for the panel (and all older copies)
-                panel(g / NK);
-                window(g + BSTAGES - 1);
-                wait_vm<WIN>();
-                barrier();
-            } else {
-                window(g + BSTAGES - 1);
-            }
+            // The next row block's panel, one pair stage at a time as the old
+            // one's free up: pair p is last read in K-tiles 2p, 2p+1 of a
+            // row block's last tile, so after publish(2p+2) it is free (p <
+            // NK/2-1 in that tile, the last pair after publish(0) of the next
+            // tile).  It is first read after publish(2p) of the next tile,
+            // which waits until at most two windows of copies are in flight;
+            // at least two were issued after the pair, and copies land in
+            // order, so the pair has landed by then: no wait of its own.
+            const int it = g / NK, kt = g - it * NK;
+            if (it + 1 < turns && (it + 1) % gn == 0 && kt >= 2 && kt % 2 == 0) pair(it + 1, kt / 2 - 1);
+            if (it < turns && it > 0 && it % gn == 0 && kt == 0) pair(it, NK / 2 - 1);
+            window(g + BSTAGES - 1);
         }
         wait_vm<0>();                      // no copy writes LDS after the workgroup ends
         return;
@@ -224,7 +220,6 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
         OutT* ctile = nullptr;
         for (int g = 0; g <= ksteps_total; ++g) {
             publish_lgkm();
-            if (new_group(g)) barrier();
             // slot (g-1) % 2 holds rows ((g-1) % NK) * RPK .. of tile (g-1)/NK - 1
             if (g >= NK + 1) {
                 const int src = g - 1;
@@ -383,7 +378,6 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
     auto step = [&]<int KT, int MODE>(int it) __attribute__((always_inline)) {
         const int g = it * NK + KT;
         publish_lgkm();
-        if (new_group(g)) barrier();
         BPT_LDS char* slot = lds + STG_BASE + (g & 1) * SLOT + wave * WSLOT;
         if constexpr (MODE == 0 && KT == 0) {
 #pragma unroll

@@ -191,12 +191,10 @@ def test_publish_waits_match_the_ring(kernels):
 def check_roles_barriers(kernels):
     """The persistent kernel with wave roles: only its copy waves issue
     copies, so only their publish waits on vmcnt, for the ring's two younger
-    windows (2 x 8 copies), and on a new A panel for the window issued after
-    it (8); the compute and store waves publish with lgkmcnt(0) alone; the
-    extra barrier of a new row block sits behind a uniform branch.  The
-    compute loop (one tile, unrolled) holds one publish per K-tile plus that
-    barrier, the copy and store loops one publish plus it; no loop with a
-    barrier writes exec."""
+    windows (2 x 8 copies; the pieces of a new A panel ride on the same
+    waits); the compute and store waves publish with lgkmcnt(0) alone.  The
+    compute loop (one tile, unrolled) holds one publish per K-tile, the copy
+    and store loops one each; no loop with a barrier writes exec."""
     seen = 0
     for n, k in kernels.items():
         if asm_info.base_name(n) != "gemm_persist_roles_kernel":
@@ -205,18 +203,15 @@ def check_roles_barriers(kernels):
         (nk,) = _ints(n)
         L = k["lines"]
         bars = [i for i, l in enumerate(L) if l == "s_barrier"]
-        allowed = {"s_waitcnt vmcnt(16) lgkmcnt(0)", "s_waitcnt lgkmcnt(0)", "s_waitcnt vmcnt(8)"}
+        allowed = {"s_waitcnt vmcnt(16) lgkmcnt(0)", "s_waitcnt lgkmcnt(0)"}
         kinds = {}
         for i in bars:
-            prev = L[i - 1]
-            if prev.startswith("s_cbranch_"):
-                prev = "branch"
-            assert prev in allowed | {"branch"}, (n, prev)
-            kinds[prev] = kinds.get(prev, 0) + 1
-        assert kinds.get("s_waitcnt vmcnt(16) lgkmcnt(0)", 0) >= 1 and kinds.get("s_waitcnt vmcnt(8)", 0) == 1, kinds
+            assert L[i - 1] in allowed, (n, L[i - 1])
+            kinds[L[i - 1]] = kinds.get(L[i - 1], 0) + 1
+        assert kinds.get("s_waitcnt vmcnt(16) lgkmcnt(0)", 0) >= 1, kinds
         per_loop = sorted(sum(1 for i in lp if L[i] == "s_barrier") for lp in _loops(L)
                           if any(L[i] == "s_barrier" for i in lp))
-        assert per_loop == [2, 2, nk + 1], (n, per_loop)
+        assert per_loop == [1, 1, nk], (n, per_loop)
         for lp in _loops(L):
             if any(L[i] == "s_barrier" for i in lp):
                 writes = [L[i] for i in sorted(lp) if _EXEC_WRITE.match(L[i])]
