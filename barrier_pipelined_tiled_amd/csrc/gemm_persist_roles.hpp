@@ -231,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
                     const int part = 2 * sw + x / RD, h = x % RD;
                     const int r2 = h * 8 + lane / 8;
                     const int4_t u = *(const BPT_LDS int4_t*)(s + part * WSLOT + stg_chunk(r2, lane % 8));
-                    const bool swapped = RPK == 32 ? (r2 & 16) != 0 : (lane % 8) % 2 != 0;
+                    const bool swapped = (((RPK == 32 ? r2 >> 4 : lane % 8) ^ r2) & 1) != 0;
                     v[x] = swapped ? int4_t{u[2], u[3], u[0], u[1]} : u;
                 }
                 if (it != c_it) {
@@ -304,19 +304,24 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
     static_assert(MB + 2 * NB == NMMA, "one fragment read per MFMA");
 
     // The held rows of step KS (RPK rows from KS*RPK on) into this wave's
-    // part of slot `sb`; the layout and the order of writes are the
-    // A-resident kernel's (gemm_persist_ares.hpp): lane l holds row
-    // PM*32 + l%32, 16-byte chunk nb*4 + g of the 128-byte row, 8-byte half
-    // l/32; slot row r goes to chunk q ^ ((r >> 1) & 7), and with RPK = 16 a
-    // v_permlane16_swap of chunks 2p and 2p+1 first puts the step's 16 rows
-    // into one register of all 64 lanes.
+    // part of slot `sb`; the order of writes is the A-resident kernel's
+    // (gemm_persist_ares.hpp): lane l holds row PM*32 + l%32, 16-byte chunk
+    // nb*4 + g of the 128-byte row, 8-byte half l/32; slot row r goes to
+    // chunk q ^ ((r >> 1) & 7), and with RPK = 16 a v_permlane16_swap of
+    // chunks 2p and 2p+1 first puts the step's 16 rows into one register of
+    // all 64 lanes.  The two 8-byte halves of a chunk trade places on odd
+    // rows: an 8-byte LDS write serves 16 lanes per cycle over 128 bytes of
+    // banks, so the 16 rows of one write must land on 16 distinct 8-byte
+    // positions modulo 128 bytes (the chunk swizzle alone gives 8, and a
+    // write took twice its cycles under SQ_LDS_BANK_CONFLICT).
     auto stg_chunk = [](int r, int q) __attribute__((always_inline)) { return r * 128 + ((q ^ ((r >> 1) & 7)) * 16); };
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     auto stage_write = [&]<int KS>(BPT_LDS char* slot, int x) __attribute__((always_inline)) {
         constexpr int PM = KS * RPK / 32, H = (KS * RPK % 32) / 16;
         if constexpr (RPK == 32) {
             const int nb = x / 4, g = x % 4, r = lane % 32;
-            *(BPT_LDS out4_t*)(slot + stg_chunk(r, nb * 4 + g) + ((lane / 32) ^ ((r >> 4) & 1)) * 8) = held[PM][nb][g];
+            *(BPT_LDS out4_t*)(slot + stg_chunk(r, nb * 4 + g) + ((lane / 32) ^ ((r >> 4) & 1) ^ (r & 1)) * 8) =
+                held[PM][nb][g];
         } else {
             if (H == 0 && x < NB) {
 #pragma unroll
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void gemm_persist_roles_kernel(GemmArgs arg
             if (x >= 2 && x < 2 + 2 * NB) {
                 const int nb = (x - 2) / 2, p = (x - 2) % 2;
                 const int r = lane % 16, q = nb * 4 + 2 * p + (lane / 16) % 2;
-                *(BPT_LDS out4_t*)(slot + stg_chunk(r, q) + ((lane / 32) ^ (q & 1)) * 8) = held[PM][nb][2 * p + H];
+                *(BPT_LDS out4_t*)(slot + stg_chunk(r, q) + ((lane / 32) ^ (q & 1) ^ (r & 1)) * 8) = held[PM][nb][2 * p + H];
             }
         }
     };
